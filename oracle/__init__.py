@@ -1,0 +1,20 @@
+"""fp64 CPU oracle for the exact attention forward (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It shares no code with the HIP library.
+"""
+from .exact import (  # noqa: F401
+    admissible_mask,
+    attention,
+    attention_rows,
+    attention_varlen,
+    decode,
+    head_attention,
+    kv_head,
+    weighted_values,
+    merge_partials,
+    scores,
+    softmax_rows,
+    tiled_online_attention,
+    to_f64,
+)
