@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Throughput of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+
+One step is one pass of the hot path over the batched-MHA workload
+(B=4, H=16, N=2048, d=128, bf16, scale 1/sqrt(128)) in both of its modes,
+non-causal then causal.  ``value`` is the step's algorithmic TFLOP/s
+(4*B*H*Nq*Nk*d, halved for the causal pass) with inputs already resident in
+device memory.  ``roofline`` reports the dominant kernel (the non-causal
+forward) against the MI355X dense bf16 MFMA peak, timed with HIP events on the
+launch stream.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded
+sample of the same workload.  ``other_workloads`` adds the long causal GQA,
+varlen and split-KV decode workloads (TFLOP/s, or GB/s for decode).
+
+Prints exactly one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+METRIC = "attention fwd TFLOP/s (4·B·H·Nq·Nk·d, causal halved) and % of bf16 MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "exact_attention_84_amd", "csrc")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def to_dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class LaunchTimer:
+    """HIP-event timing of individual launches on torch's current stream (the
+    stream the library launches on)."""
+
+    def __init__(self):
+        self.pairs = {}
+
+    def run(self, name, fn):
+        import torch
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.pairs.setdefault(name, []).append((a, b))
+
+    def avg_ms(self, name):
+        ps = self.pairs.get(name, [])
+        return sum(a.elapsed_time(b) for a, b in ps) / max(1, len(ps))
+
+
+def time_calls(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def other_workloads(fa, steps, warmup):
+    import torch
+    res = {}
+    for wid in (3, 4):
+        w = W.WORKLOADS[wid]
+        inp = W.make_workload(w, seed=0)
+        q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+        kw = {}
+        if w.kind == "varlen":
+            cu = torch.from_numpy(inp["cu_q"]).cuda()
+            kw = dict(cu_seqlens_q=cu, cu_seqlens_k=cu, max_seqlen_q=int(inp["lengths"].max()),
+                      max_seqlen_k=int(inp["lengths"].max()))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+        ms = time_calls(lambda: fa.attention(q, k, v, causal=True, scale=w.scale, out=o, lse=lse,
+                                             **kw), steps, warmup)
+        fl = W.flops(w, inp.get("lengths"))
+        tf = fl / (ms * 1e-3) / 1e12
+        res[w.name] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                       "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "gflop": round(fl / 1e9, 1)}
+        log(w.name, res[w.name])
+        del q, k, v, o, lse
+    w = W.WORKLOADS[5]
+    lens = W.workload_lengths(w, seed=0)
+    qd = to_dev(W.decode_q(w.batch, w.heads_q, w.head_dim, seed=0, wid=w.wid))
+    kc = torch.zeros((w.batch, w.seqlen_k, w.heads_kv, w.head_dim), dtype=torch.bfloat16,
+                     device="cuda")
+    vc = torch.zeros_like(kc)
+    for b in range(w.batch):
+        kb, vb = W.decode_kv_slice(b, int(lens[b]), w.heads_kv, w.head_dim, seed=0, wid=w.wid)
+        kc[b, :int(lens[b])] = to_dev(kb)
+        vc[b, :int(lens[b])] = to_dev(vb)
+    lensd = torch.from_numpy(lens).cuda()
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.batch, w.heads_q), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.decode_workspace_size(w.batch, w.heads_q, w.seqlen_k, w.head_dim),
+                     dtype=torch.uint8, device="cuda")
+    ms = time_calls(lambda: fa.decode(qd, kc, vc, lensd, scale=w.scale, out=o, lse=lse,
+                                      workspace=ws), steps, warmup)
+    by = W.decode_bytes(w, lens)
+    gbs = by / (ms * 1e-3) / 1e9
+    res[w.name] = {"ms": round(ms, 4), "gbs": round(gbs, 1),
+                   "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4), "gbytes": round(by / 1e9, 3)}
+    log(w.name, res[w.name])
+    return res
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The fp64 oracle on (sequence, head) slices of the workload, both modes,
+    until the time budget is spent."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    q, k, v = W.make_fixed(1, w.heads_q, w.heads_kv, w.seqlen_q, w.seqlen_k, w.head_dim, seed=0,
+                           wid=w.wid)
+    done_flops, heads = 0.0, 0
+    t0 = time.perf_counter()
+    for h in range(w.heads_q):
+        qh, kh, vh = (oracle.to_f64(x[0, :, h]) for x in (q, k, v))
+        for causal in (False, True):
+            oracle.head_attention(qh, kh, vh, w.scale, causal)
+            done_flops += (0.5 if causal else 1.0) * 4.0 * w.seqlen_q * w.seqlen_k * w.head_dim
+        heads += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads} of {w.batch * w.heads_q} (sequence, head) slices of "
+                      f"{w.name}, non-causal and causal, fp64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(the attention forward here runs whole on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_84_amd as fa
+    fa.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    props = torch.cuda.get_device_properties(0)
+    log("device", props.name, getattr(props, "gcnArchName", ""), "CUs",
+        props.multi_processor_count)
+
+    w = W.WORKLOADS[2]
+    inp = W.make_workload(w, seed=0)
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    o_nc, o_c = torch.empty_like(q), torch.empty_like(q)
+    lse_nc = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+    lse_c = torch.empty_like(lse_nc)
+    fl_nc = W.flops(w, causal=False)
+    fl_c = W.flops(w, causal=True)
+
+    timer = LaunchTimer()
+
+    def step(t=None):
+        if t is None:
+            fa.attention(q, k, v, causal=False, scale=w.scale, out=o_nc, lse=lse_nc)
+            fa.attention(q, k, v, causal=True, scale=w.scale, out=o_c, lse=lse_c)
+        else:
+            t.run("noncausal", lambda: fa.attention(q, k, v, causal=False, scale=w.scale,
+                                                    out=o_nc, lse=lse_nc))
+            t.run("causal", lambda: fa.attention(q, k, v, causal=True, scale=w.scale,
+                                                 out=o_c, lse=lse_c))
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(a.steps):
+        step(timer)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / a.steps
+    assert torch.isfinite(o_nc.float()).all() and torch.isfinite(o_c.float()).all()
+    value = (fl_nc + fl_c) / (ms_step * 1e-3) / 1e12
+    ms_nc, ms_c = timer.avg_ms("noncausal"), timer.avg_ms("causal")
+    ach = fl_nc / (ms_nc * 1e-3) / 1e12
+    log(f"step {ms_step:.4f} ms ({wall / a.steps * 1e3:.4f} ms wall), non-causal {ms_nc:.4f} ms "
+        f"({ach:.1f} TFLOP/s), causal {ms_c:.4f} ms ({fl_c / (ms_c * 1e-3) / 1e12:.1f} TFLOP/s)")
+
+    kname = "fwd_kernel<128, 4, 1, false>"
+    traffic = measured_traffic("fwd_noncausal_d128")
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name + " (non-causal + causal)", "batch": w.batch,
+                   "heads_q": w.heads_q, "heads_kv": w.heads_kv, "seq_len": w.seqlen_q,
+                   "head_dim": w.head_dim, "scale": round(w.scale, 6),
+                   "inputs": "bf16 N(0,1), seed 0", "o_dtype": "bf16"},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "kernel": kname, "achieved": round(ach, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "avg_launch_ms": round(ms_nc, 5),
+                     "flop_per_launch": fl_nc},
+        "causal_launch": {"avg_launch_ms": round(ms_c, 5),
+                          "tflops": round(fl_c / (ms_c * 1e-3) / 1e12, 2)},
+    }
+    del o_nc, o_c, lse_nc, lse_c
+    if not a.no_extra:
+        res["other_workloads"] = other_workloads(fa, max(5, a.steps // 5), 3)
+    if not a.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w)
+        log("cpu_baseline", res["cpu_baseline"])
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res, ensure_ascii=False), flush=True)
+
+
+if __name__ == "__main__":
+    main()

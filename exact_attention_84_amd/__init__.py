@@ -1,0 +1,176 @@
+"""Fused exact-attention forward for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libfa.so`` (include/fa.h).  torch is
+used only to own device memory and to name the current stream; every step of
+the computation runs in the library's HIP kernels.
+
+    o, lse = attention(q, k, v, causal=True)                      # [B,N,H,d]
+    o, lse = attention(q, k, v, causal=True, cu_seqlens_q=cu,     # packed
+                       max_seqlen_q=n_max)
+    o, lse = decode(q, k_cache, v_cache, cache_seqlens)           # split-KV
+    o, lse = combine(o_part, lse_part)                            # LSE merge
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from ._lib import FA_DTYPE_BF16, FA_DTYPE_F32, FaError, check, load
+
+__all__ = ["attention", "decode", "combine", "decode_workspace_size", "FaError", "load"]
+
+_OUT_DTYPES = {torch.bfloat16: FA_DTYPE_BF16, torch.float32: FA_DTYPE_F32}
+
+
+def _stream_handle(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+
+
+def attention(q, k, v, *, causal: bool = False, scale: float | None = None,
+              cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q: int | None = None,
+              max_seqlen_k: int | None = None, out=None, lse=None,
+              out_dtype=torch.bfloat16, stream=None):
+    """softmax(q k^T * scale) v and its row logsumexp.
+
+    Fixed length: q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] -> o [B, Nq, Hq, d],
+    lse [B, Nq, Hq].  Packed (cu_seqlens_q given, int32 [n+1]): q [Tq, Hq, d],
+    k/v [Tk, Hkv, d] -> o [Tq, Hq, d], lse [Tq, Hq]; max_seqlen_q/k must bound
+    the sequence lengths (read from the offsets on the host when omitted).
+    """
+    lib = load()
+    varlen = cu_seqlens_q is not None
+    ndim = 3 if varlen else 4
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, ndim)
+    if out_dtype not in _OUT_DTYPES:
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    d = q.shape[-1]
+    if k.shape[-1] != d:
+        raise ValueError("q and k head dims differ")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if varlen:
+        _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+        if cu_seqlens_k is not None:
+            _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+        batch = cu_seqlens_q.numel() - 1
+        if max_seqlen_q is None:
+            max_seqlen_q = int(torch.diff(cu_seqlens_q).max().item()) if batch > 0 else 0
+        if max_seqlen_k is None:
+            ck = cu_seqlens_q if cu_seqlens_k is None else cu_seqlens_k
+            max_seqlen_k = int(torch.diff(ck).max().item()) if batch > 0 else 0
+        hq, hkv = q.shape[1], k.shape[1]
+        nq, nk = 0, 0
+        lse_shape = (q.shape[0], hq)
+    else:
+        batch, nq, hq, _ = q.shape
+        nk, hkv = k.shape[1], k.shape[2]
+        if k.shape[0] != batch:
+            raise ValueError("q and k batch sizes differ")
+        max_seqlen_q = max_seqlen_k = 0
+        lse_shape = (batch, nq, hq)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    else:
+        _need(out, "out", out_dtype, ndim)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    if lse is None:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    else:
+        _need(lse, "lse", torch.float32)
+        if tuple(lse.shape) != lse_shape:
+            raise ValueError(f"lse must have shape {lse_shape}")
+    st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), batch, hq, hkv, nq, nk, d,
+                    scale, int(bool(causal)), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                    int(max_seqlen_q), int(max_seqlen_k), _OUT_DTYPES[out_dtype],
+                    _stream_handle(stream))
+    check(st, "fa_fwd")
+    return out, lse
+
+
+def decode_workspace_size(batch: int, heads_q: int, max_cache_len: int, head_dim: int,
+                          chunk: int = 0) -> int:
+    return int(load().fa_decode_workspace_size(batch, heads_q, max_cache_len, head_dim, chunk))
+
+
+def decode(q, k_cache, v_cache, cache_seqlens, *, scale: float | None = None, chunk: int = 0,
+           out=None, lse=None, workspace=None, out_dtype=torch.bfloat16, stream=None):
+    """One query per sequence against a KV cache, split over key chunks.
+
+    q [B, Hq, d]; k_cache/v_cache [B, Ncache, Hkv, d]; cache_seqlens int32 [B]
+    -> o [B, Hq, d], lse [B, Hq].  ``workspace`` (uint8 device tensor) is
+    allocated when omitted.
+    """
+    lib = load()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    if out_dtype not in _OUT_DTYPES:
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    batch, hq, d = q.shape
+    if k_cache.shape != v_cache.shape or k_cache.shape[0] != batch or k_cache.shape[3] != d:
+        raise ValueError("cache shapes do not match q")
+    if cache_seqlens.numel() != batch:
+        raise ValueError("cache_seqlens must have one entry per sequence")
+    ncache, hkv = k_cache.shape[1], k_cache.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = lib.fa_decode_workspace_size(batch, hq, ncache, d, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _need(workspace, "workspace", torch.uint8)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    else:
+        _need(out, "out", out_dtype, 3)
+    if lse is None:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
+    else:
+        _need(lse, "lse", torch.float32, 2)
+    st = lib.fa_fwd_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
+                                   _ptr(out), _ptr(lse), batch, hq, hkv, ncache, d, scale,
+                                   int(chunk), _ptr(workspace), workspace.numel(),
+                                   _OUT_DTYPES[out_dtype], _stream_handle(stream))
+    check(st, "fa_fwd_decode_splitkv")
+    return out, lse
+
+
+def combine(o_part, lse_part, *, out=None, lse=None, out_dtype=torch.float32, stream=None):
+    """LSE-weighted merge: o_part [rows, S, d] fp32, lse_part [rows, S] fp32
+    (-inf = empty split) -> o [rows, d], lse [rows]."""
+    lib = load()
+    _need(o_part, "o_part", torch.float32, 3)
+    _need(lse_part, "lse_part", torch.float32, 2)
+    rows, n_splits, d = o_part.shape
+    if tuple(lse_part.shape) != (rows, n_splits):
+        raise ValueError("lse_part must be [rows, n_splits]")
+    if out is None:
+        out = torch.empty((rows, d), dtype=out_dtype, device=o_part.device)
+    if lse is None:
+        lse = torch.empty((rows,), dtype=torch.float32, device=o_part.device)
+    st = lib.fa_combine(_ptr(o_part), _ptr(lse_part), rows, n_splits, d, _ptr(out), _ptr(lse),
+                        _OUT_DTYPES[out_dtype], _stream_handle(stream))
+    check(st, "fa_combine")
+    return out, lse

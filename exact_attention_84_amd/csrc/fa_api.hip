@@ -1,0 +1,262 @@
+// C ABI of the attention library: argument validation, launch parameters,
+// dispatch.  Every argument is checked before any HIP call, so invalid calls
+// return their status without touching the device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/fa.h"
+#include "fa_internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+fa_status fail(fa_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+fa_status fail(fa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+fa_status ok() {
+  g_last_error[0] = '\0';
+  return FA_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+// The kernels use gfx950-only instructions (v_mfma_f32_32x32x16_bf16,
+// v_cvt_pk_bf16_f32); refuse any other device.
+fa_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_ARCH, "device index %d unsupported", dev);
+  int state = g_arch_state[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(FA_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    state = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_state[dev].store(state, std::memory_order_relaxed);
+    if (state == 2) return fail(FA_ERR_ARCH, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  }
+  if (state != 1) return fail(FA_ERR_ARCH, "device %d is not gfx950", dev);
+  return FA_OK;
+}
+
+bool valid_head_dim(int d) { return d == 64 || d == 128; }
+
+bool valid_scale(float s) { return isfinite(s) && s > 0.f; }
+
+constexpr long long kMaxElems = 1LL << 40;  // sanity bound on any one tensor
+
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+int default_decode_chunk(int batch, int heads_kv, int max_cache_len) {
+  // Enough workgroups to fill 256 CUs several times over, chunks of at least
+  // 512 keys so the per-chunk partials stay a small fraction of the traffic.
+  const long long units = (long long)batch * heads_kv;
+  const long long want = 8192;
+  long long splits = (want + units - 1) / (units > 0 ? units : 1);
+  if (splits < 1) splits = 1;
+  int chunk = (int)((max_cache_len + splits - 1) / splits);
+  chunk = round_up(chunk < 512 ? 512 : chunk, fa::kDecodeTile);
+  return chunk;
+}
+
+int decode_splits(int max_cache_len, int chunk) {
+  const int s = (max_cache_len + chunk - 1) / chunk;
+  return s < 1 ? 1 : s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE";
+    case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM";
+    case FA_ERR_GQA: return "FA_ERR_GQA";
+    case FA_ERR_DTYPE: return "FA_ERR_DTYPE";
+    case FA_ERR_ARCH: return "FA_ERR_ARCH";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+    case FA_ERR_ARG: return "FA_ERR_ARG";
+  }
+  return "FA_ERR_UNKNOWN";
+}
+
+const char* fa_last_error(void) { return g_last_error; }
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                 int heads_q, int heads_kv, int seqlen_q, int seqlen_k, int head_dim,
+                 float scale, int causal, const int32_t* cu_seqlens_q,
+                 const int32_t* cu_seqlens_k, int max_seqlen_q, int max_seqlen_k,
+                 fa_dtype o_dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return fail(FA_ERR_NULL, "q, k, v, o and lse must be non-NULL");
+  if (!valid_head_dim(head_dim))
+    return fail(FA_ERR_HEADDIM, "head_dim %d not supported (64 or 128)", head_dim);
+  if (batch < 0 || heads_q <= 0 || heads_kv <= 0)
+    return fail(FA_ERR_SHAPE, "batch >= 0 and heads > 0 required (batch %d, heads %d/%d)", batch,
+                heads_q, heads_kv);
+  if (heads_q % heads_kv)
+    return fail(FA_ERR_GQA, "heads_kv %d does not divide heads_q %d", heads_kv, heads_q);
+  if (!valid_scale(scale)) return fail(FA_ERR_ARG, "scale must be finite and > 0");
+  if (causal != 0 && causal != 1) return fail(FA_ERR_ARG, "causal must be 0 or 1");
+  if (o_dtype != FA_DTYPE_BF16 && o_dtype != FA_DTYPE_F32)
+    return fail(FA_ERR_DTYPE, "o_dtype %d unknown", (int)o_dtype);
+  const bool varlen = cu_seqlens_q != nullptr;
+  int rows_q, rows_k;
+  if (varlen) {
+    if (max_seqlen_q < 0 || max_seqlen_k < 0)
+      return fail(FA_ERR_SHAPE, "max_seqlen_q/k must be >= 0");
+    rows_q = max_seqlen_q;
+    rows_k = max_seqlen_k;
+  } else {
+    if (seqlen_q < 0 || seqlen_k < 0) return fail(FA_ERR_SHAPE, "seqlen_q/k must be >= 0");
+    rows_q = seqlen_q;
+    rows_k = seqlen_k;
+  }
+  if ((long long)batch * rows_q * heads_q * head_dim > kMaxElems ||
+      (long long)batch * rows_k * heads_kv * head_dim > kMaxElems)
+    return fail(FA_ERR_SHAPE, "tensor too large");
+  const int br = fa::fwd_block_rows(head_dim);
+  const long long n_qtiles = (rows_q + br - 1) / br;
+  const long long total = (long long)batch * heads_q * n_qtiles;
+  if (total > 0x7fffffffLL) return fail(FA_ERR_SHAPE, "too many query tiles");
+  if (total == 0) return ok();  // nothing to compute
+
+  fa_status s = check_device();
+  if (s != FA_OK) return s;
+
+  fa::FwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = o;
+  p.lse = lse;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = varlen ? (cu_seqlens_k ? cu_seqlens_k : cu_seqlens_q) : nullptr;
+  p.hq = heads_q;
+  p.hkv = heads_kv;
+  p.group = heads_q / heads_kv;
+  p.seqlen_q = seqlen_q;
+  p.seqlen_k = seqlen_k;
+  p.n_qtiles = (int)n_qtiles;
+  p.total = (int)total;
+  p.c = scale * fa::kLog2eHost;
+  p.o_f32 = o_dtype == FA_DTYPE_F32;
+  hipError_t e = fa::launch_fwd(p, head_dim, causal != 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t fa_decode_workspace_size(int batch, int heads_q, int max_cache_len, int head_dim,
+                                int chunk) {
+  if (batch < 0 || heads_q <= 0 || max_cache_len < 0 || !valid_head_dim(head_dim)) return 0;
+  if (chunk < 0 || chunk % fa::kDecodeTile) return 0;
+  // The default chunk depends on heads_kv only through a larger-is-safer
+  // split count; size for the worst case (heads_kv = 1 is never larger).
+  const int c = chunk ? chunk : default_decode_chunk(batch, 1, max_cache_len);
+  const size_t splits = (size_t)decode_splits(max_cache_len, c);
+  const size_t rows = (size_t)batch * heads_q;
+  return rows * splits * ((size_t)head_dim + 1) * sizeof(float);
+}
+
+fa_status fa_fwd_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* cache_seqlens, void* o, float* lse, int batch,
+                                int heads_q, int heads_kv, int max_cache_len, int head_dim,
+                                float scale, int chunk, void* workspace, size_t workspace_bytes,
+                                fa_dtype o_dtype, void* stream) {
+  if (!q || !k_cache || !v_cache || !cache_seqlens || !o || !lse)
+    return fail(FA_ERR_NULL, "q, caches, cache_seqlens, o and lse must be non-NULL");
+  if (!valid_head_dim(head_dim))
+    return fail(FA_ERR_HEADDIM, "head_dim %d not supported (64 or 128)", head_dim);
+  if (batch < 0 || heads_q <= 0 || heads_kv <= 0 || max_cache_len < 0)
+    return fail(FA_ERR_SHAPE, "batch, max_cache_len >= 0 and heads > 0 required");
+  if (heads_q % heads_kv)
+    return fail(FA_ERR_GQA, "heads_kv %d does not divide heads_q %d", heads_kv, heads_q);
+  if (heads_q / heads_kv > fa::kDecodeMaxGroup)
+    return fail(FA_ERR_SHAPE, "heads_q / heads_kv = %d exceeds %d", heads_q / heads_kv,
+                fa::kDecodeMaxGroup);
+  if (!valid_scale(scale)) return fail(FA_ERR_ARG, "scale must be finite and > 0");
+  if (chunk < 0 || chunk % fa::kDecodeTile)
+    return fail(FA_ERR_ARG, "chunk %d must be 0 or a positive multiple of %d", chunk,
+                fa::kDecodeTile);
+  if (o_dtype != FA_DTYPE_BF16 && o_dtype != FA_DTYPE_F32)
+    return fail(FA_ERR_DTYPE, "o_dtype %d unknown", (int)o_dtype);
+  if ((long long)batch * max_cache_len * heads_kv * head_dim > kMaxElems)
+    return fail(FA_ERR_SHAPE, "cache too large");
+  const int c = chunk ? chunk : default_decode_chunk(batch, heads_kv, max_cache_len);
+  const int n_splits = decode_splits(max_cache_len, c);
+  const size_t need = fa_decode_workspace_size(batch, heads_q, max_cache_len, head_dim, c);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (reinterpret_cast<uintptr_t>(workspace) % 16)
+    return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  const long long total = (long long)batch * heads_kv * n_splits;
+  if (total > 0x7fffffffLL) return fail(FA_ERR_SHAPE, "too many splits");
+  if (batch == 0) return ok();
+
+  fa_status s = check_device();
+  if (s != FA_OK) return s;
+
+  const size_t rows = (size_t)batch * heads_q;
+  fa::DecodeParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k_cache);
+  p.v = static_cast<const uint16_t*>(v_cache);
+  p.cache_seqlens = cache_seqlens;
+  p.o_part = static_cast<float*>(workspace);
+  p.lse_part = p.o_part + rows * n_splits * head_dim;
+  p.hq = heads_q;
+  p.hkv = heads_kv;
+  p.group = heads_q / heads_kv;
+  p.cache_len = max_cache_len;
+  p.chunk = c;
+  p.n_splits = n_splits;
+  p.total = (int)total;
+  p.c = scale * fa::kLog2eHost;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = fa::launch_decode(p, head_dim, st);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  e = fa::launch_combine(p.o_part, p.lse_part, (int)rows, n_splits, head_dim, o, lse,
+                         o_dtype == FA_DTYPE_F32, st);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+fa_status fa_combine(const float* o_part, const float* lse_part, int rows, int n_splits,
+                     int head_dim, void* o, float* lse, fa_dtype o_dtype, void* stream) {
+  if (!o_part || !lse_part || !o || !lse)
+    return fail(FA_ERR_NULL, "o_part, lse_part, o and lse must be non-NULL");
+  if (!valid_head_dim(head_dim))
+    return fail(FA_ERR_HEADDIM, "head_dim %d not supported (64 or 128)", head_dim);
+  if (rows < 0 || n_splits < 1 || n_splits > fa::kCombineMaxSplits)
+    return fail(FA_ERR_SHAPE, "rows >= 0 and 1 <= n_splits <= %d required",
+                fa::kCombineMaxSplits);
+  if (o_dtype != FA_DTYPE_BF16 && o_dtype != FA_DTYPE_F32)
+    return fail(FA_ERR_DTYPE, "o_dtype %d unknown", (int)o_dtype);
+  if (rows == 0) return ok();
+  fa_status s = check_device();
+  if (s != FA_OK) return s;
+  hipError_t e = fa::launch_combine(o_part, lse_part, rows, n_splits, head_dim, o, lse,
+                                    o_dtype == FA_DTYPE_F32, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,212 @@
+// Split-KV decode (one query per sequence against a KV cache) and the
+// LSE-weighted combine of partial results.
+//
+// The G = Hq / Hkv query heads that share a key/value head are folded into the
+// query-row dimension ("FlashAttention — IO 感知的精确注意力 kernel", section
+// 4: at decode time with grouped heads, the group dimension is reshaped into
+// the sequence dimension), so one workgroup serves a whole group from a single
+// read of its keys.  The cache of each sequence is cut into chunks processed
+// by separate workgroups (split-KV for a short query against long keys, same
+// page, section 2.3 step 3); each chunk writes its normalised partial output
+// and logsumexp, and a second kernel merges them by LSE weight (the block
+// merge of the PKU lecture notes "FlashAttention", section 6: only the
+// running max, sum and output of each part are kept).
+#include "fa_device.hpp"
+#include "fa_internal.hpp"
+
+namespace fa {
+
+template <int D>
+__global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_kernel(const DecodeParams p) {
+  constexpr int BC = kDecodeTile;
+  constexpr int T = kDecodeWaves * 64;
+  static_assert(BC == 32 * kDecodeWaves, "one 32-key sub-tile per wave");
+  using Loader = TileLoader<D, BC, T>;
+  constexpr int KSTR = Loader::KSTR;
+  constexpr int SMEM = Loader::K_ELEMS + Loader::VT_ELEMS;
+  static_assert((kDecodeWaves * kDecodeMaxGroup * (D + 2)) * 4 <= SMEM * 2,
+                "cross-wave merge must fit in the K/V staging area");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
+  uint16_t* k_lds = smem;
+  uint16_t* vt_lds = smem + Loader::K_ELEMS;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int m32 = lane & 31, hh = lane >> 5;
+
+  int item = blockIdx.x;
+  const int split = item % p.n_splits;
+  item /= p.n_splits;
+  const int kvh = item % p.hkv;
+  const int b = item / p.hkv;
+  const int G = p.group;
+  // Lengths are clamped to the cache so that a bad length cannot read past it.
+  const int Lk = min(max(p.cache_seqlens[b], 0), p.cache_len);
+  const int kbeg = split * p.chunk;
+  const int kend = min(Lk, kbeg + p.chunk);
+  const size_t row0 = (size_t)b * p.hq + (size_t)kvh * G;  // output row of head kvh*G
+  if (kbeg >= kend) {
+    if (tid < G) p.lse_part[(row0 + tid) * p.n_splits + split] = -INFINITY;
+    return;
+  }
+
+  const size_t kv_stride = (size_t)p.hkv * D;
+  const size_t kv_off = (size_t)b * p.cache_len * kv_stride + (size_t)kvh * D;
+  const uint16_t* kbase = p.k + kv_off;
+  const uint16_t* vbase = p.v + kv_off;
+
+  WaveState<D, 1> st;
+  st.init();
+  {
+    const uint16_t* qp = p.q + (row0 + m32) * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (m32 < G) raw = *reinterpret_cast<const u32x4*>(qp + 16 * s);
+      st.qf[0][s] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+
+  Loader ld;
+  ld.load(kbase, vbase, kv_stride, kbeg, kend, tid);
+  for (int k0 = kbeg; k0 < kend; k0 += BC) {
+    __syncthreads();
+    ld.store(k_lds, vt_lds, tid);
+    __syncthreads();
+    if (k0 + BC < kend) ld.load(kbase, vbase, kv_stride, k0 + BC, kend, tid);
+
+    const int ksub = k0 + wave * 32;  // this wave's 32 keys of the tile
+    if (ksub < kend) {
+      f32x16 s[1][1];
+      scores_subtile<D, 1, KSTR>(s[0], k_lds, wave, st.qf, m32, hh);
+      if (ksub + 32 > kend) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (ksub + acc_row(v, hh) >= kend) s[0][0][v] = -INFINITY;
+      }
+      bf16x8 pb[1][1][2];
+      softmax_update<D, 1, 1>(st, s, pb, p.c);
+      pv_subtile<D, 1, BC>(st, vt_lds, wave, pb[0], m32, hh);
+    }
+  }
+
+  // ---- merge the four waves' key subsets, then write this chunk's partial ----
+  __syncthreads();  // the K/V staging area becomes the merge buffer
+  float* red_o = reinterpret_cast<float*>(smem);         // [waves][G][D]
+  float* red_m = red_o + kDecodeWaves * G * D;           // [waves][G]
+  float* red_l = red_m + kDecodeWaves * G;               // [waves][G]
+  const float lt = halfwave_sum(st.l[0]);
+  if (m32 < G) {
+    float* ro = red_o + (wave * G + m32) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) ro[dt * 32 + acc_row(v, hh)] = st.o[0][dt][v];
+    if (hh == 0) {
+      red_m[wave * G + m32] = st.mc[0];
+      red_l[wave * G + m32] = lt;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += T) {
+    const int n = idx / D, d = idx % D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) mx = fmaxf(mx, red_m[w * G + n]);
+    const float msub = mx == -INFINITY ? 0.f : mx;
+    float lsum = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      const float f = fast_exp2(red_m[w * G + n] - msub);
+      lsum += f * red_l[w * G + n];
+      acc += f * red_o[(w * G + n) * D + d];
+    }
+    const size_t row = row0 + n;
+    p.o_part[(row * p.n_splits + split) * D + d] = lsum > 0.f ? acc / lsum : 0.f;
+    if (d == 0)
+      p.lse_part[row * p.n_splits + split] =
+          lsum > 0.f ? (mx + __log2f(lsum)) * kLn2 : -INFINITY;
+  }
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// One wave per output row: M = max_s lse_s, lse = M + ln sum_s exp(lse_s - M),
+// o = sum_s exp(lse_s - lse) o_s over the non-empty splits.
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
+                                                      const float* __restrict__ lse_part, int rows,
+                                                      int n_splits, void* o, float* lse,
+                                                      int o_f32) {
+  constexpr int PER = D / 64;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float* lp = lse_part + (size_t)row * n_splits;
+  float mx = -INFINITY;
+  for (int s = lane; s < n_splits; s += 64) mx = fmaxf(mx, lp[s]);
+  mx = wave_max(mx);
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float out_lse = -INFINITY;
+  if (mx != -INFINITY) {
+    float sum = 0.f;
+    for (int s = lane; s < n_splits; s += 64) {
+      const float x = lp[s];
+      sum += (x == -INFINITY) ? 0.f : expf(x - mx);
+    }
+    sum = wave_sum(sum);
+    out_lse = mx + logf(sum);
+    const float* op = o_part + (size_t)row * n_splits * D + lane * PER;
+    for (int s = 0; s < n_splits; ++s) {
+      const float x = lp[s];
+      if (x == -INFINITY) continue;
+      const float w = expf(x - out_lse);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] += w * op[(size_t)s * D + e];
+    }
+  }
+  if (o_f32) {
+    float* dst = reinterpret_cast<float*>(o) + (size_t)row * D + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) dst[e] = acc[e];
+  } else {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(o) + (size_t)row * D + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; e += 2) *reinterpret_cast<uint32_t*>(dst + e) = pack_bf16x2(acc[e], acc[e + 1]);
+  }
+  if (lane == 0) lse[row] = out_lse;
+}
+
+hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream) {
+  if (head_dim == 128)
+    hipLaunchKernelGGL(decode_kernel<128>, dim3(p.total), dim3(kDecodeWaves * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(decode_kernel<64>, dim3(p.total), dim3(kDecodeWaves * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* o_part, const float* lse_part, int rows, int n_splits,
+                          int head_dim, void* o, float* lse, int o_f32, hipStream_t stream) {
+  const dim3 grid((rows + 3) / 4);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(256), 0, stream, o_part, lse_part, rows,
+                       n_splits, o, lse, o_f32);
+  else
+    hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(256), 0, stream, o_part, lse_part, rows,
+                       n_splits, o, lse, o_f32);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,65 @@
+// Host <-> kernel interface of the attention library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Prefill tile shape: kFwdWaves waves per workgroup, each owning kFwdNT
+// groups of 32 query rows; K/V tiles of 64 keys.
+#ifndef FA_FWD_WAVES
+#define FA_FWD_WAVES 4
+#endif
+#ifndef FA_FWD_NT
+#define FA_FWD_NT 1
+#endif
+constexpr int kFwdWaves = FA_FWD_WAVES;
+constexpr int kFwdNT = FA_FWD_NT;
+
+// Split-KV decode: a workgroup of 4 waves takes 128 keys per step, 32 per wave.
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeTile = 128;
+constexpr int kDecodeMaxGroup = 32;
+constexpr int kCombineMaxSplits = 4096;
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  void* o;
+  float* lse;
+  const int32_t* cu_q;  // NULL: fixed-length batch
+  const int32_t* cu_k;
+  int hq, hkv, group;
+  int seqlen_q, seqlen_k;  // fixed-length mode
+  int n_qtiles;            // query tiles per (sequence, head)
+  int total;               // workgroups
+  float c;                 // scale * log2(e)
+  int o_f32;
+};
+
+struct DecodeParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* cache_seqlens;
+  float* o_part;    // [B*Hq][n_splits][D]
+  float* lse_part;  // [B*Hq][n_splits]
+  int hq, hkv, group;
+  int cache_len;
+  int chunk;
+  int n_splits;
+  int total;  // B * Hkv * n_splits
+  float c;
+};
+
+int fwd_block_rows(int head_dim);
+hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_combine(const float* o_part, const float* lse_part, int rows, int n_splits,
+                          int head_dim, void* o, float* lse, int o_f32, hipStream_t stream);
+
+}  // namespace fa

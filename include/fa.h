@@ -1,0 +1,161 @@
+/*
+ * fa.h -- C ABI of the fused exact-attention forward for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Computes O = softmax(Q K^T * scale) V and the per-row natural-log
+ * logsumexp LSE = ln sum_j exp(scale * <q_i, k_j>) in one fused tiled pass:
+ * the N x N scores and probabilities never reach device memory.  The result is
+ * the plain definition ("推理优化 | FlashAttention 1-4 详解", section
+ * 原算法：标准 Attention 与显存瓶颈), reached with the online-softmax
+ * recurrence of the same page (section Online Softmax 数学推导) and the
+ * outputs named on "FlashAttention — IO 感知的精确注意力 kernel" (section 2.3,
+ * step 5: O and the logsumexp are written back, nothing N x N).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is caller-owned DEVICE memory on the current HIP
+ *     device.  The library never allocates or frees memory and keeps no state
+ *     besides a per-device cache of the architecture check.
+ *   - Inputs q, k, v (and the KV caches) are bfloat16, contiguous, with the
+ *     head dimension innermost.  O is bfloat16 or float32 (fa_dtype); LSE is
+ *     float32.
+ *   - head_dim must be 64 or 128.  heads_kv must divide heads_q: query head h
+ *     reads key/value head h / (heads_q / heads_kv) (grouped-query attention,
+ *     "FlashAttention — IO 感知的精确注意力 kernel", section 1 capability table).
+ *   - Causal masking is bottom-right aligned: query i of a sequence with Lq
+ *     queries and Lk keys sees key j when j <= i + Lk - Lq (the lower triangle
+ *     when Lq == Lk).  A query row that sees no key gets O = 0, LSE = -inf.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  They return after enqueueing.  Device faults surface at the
+ *     caller's next synchronisation.
+ *   - Errors: every argument is validated before anything is enqueued; on a
+ *     non-FA_OK return nothing was launched and outputs are untouched (except
+ *     FA_ERR_HIP, which reports a failed launch).  fa_last_error() gives a
+ *     detail string for the calling thread.
+ *   - Thread safety: entry points are reentrant; the detail string is
+ *     thread-local.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  FA_ERR_SHAPE = 2,     /* a size is non-positive, too large, or inconsistent */
+  FA_ERR_HEADDIM = 3,   /* head_dim is not 64 or 128                         */
+  FA_ERR_GQA = 4,       /* heads_kv does not divide heads_q                  */
+  FA_ERR_DTYPE = 5,     /* unknown output dtype                              */
+  FA_ERR_ARCH = 6,      /* the current device is not gfx950                  */
+  FA_ERR_WORKSPACE = 7, /* workspace NULL or smaller than required           */
+  FA_ERR_HIP = 8,       /* a HIP runtime call or launch failed               */
+  FA_ERR_ARG = 9        /* another argument is out of range (scale, chunk)   */
+} fa_status;
+
+typedef enum fa_dtype {
+  FA_DTYPE_BF16 = 0,
+  FA_DTYPE_F32 = 1
+} fa_dtype;
+
+/*
+ * fa_fwd -- attention forward for a batch of sequences.
+ *
+ * Fixed-length mode (cu_seqlens_q == NULL):
+ *   q, o : [batch, seqlen_q, heads_q, head_dim]
+ *   k, v : [batch, seqlen_k, heads_kv, head_dim]
+ *   lse  : [batch, seqlen_q, heads_q]
+ *   max_seqlen_q / max_seqlen_k are ignored.
+ * Packed variable-length mode (cu_seqlens_q != NULL; "FlashAttention — IO 感知的
+ * 精确注意力 kernel", section 1: sequences packed without padding through
+ * cumulative offsets):
+ *   cu_seqlens_q : device int32 [batch + 1], non-decreasing, cu_seqlens_q[0] = 0;
+ *                  sequence s owns query rows [cu_seqlens_q[s], cu_seqlens_q[s+1]).
+ *   cu_seqlens_k : same for keys; NULL means "equal to cu_seqlens_q".
+ *   q, o : [total_q, heads_q, head_dim];  k, v : [total_k, heads_kv, head_dim]
+ *   lse  : [total_q, heads_q]
+ *   max_seqlen_q must be >= every query length (it sizes the launch);
+ *   max_seqlen_k must be >= every key length.  seqlen_q / seqlen_k are ignored.
+ *   The offsets are read on the device; they are not validated there.
+ * scale  : finite, > 0 (usually 1/sqrt(head_dim)); multiplies Q K^T in fp32.
+ * causal : 0 or 1.
+ * o_dtype: FA_DTYPE_BF16 or FA_DTYPE_F32 (O element type).
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k,
+                 int head_dim, float scale, int causal,
+                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                 int max_seqlen_q, int max_seqlen_k,
+                 fa_dtype o_dtype, void* stream);
+
+/*
+ * fa_decode_workspace_size -- bytes of float32 scratch that
+ * fa_fwd_decode_splitkv needs for these sizes (partial O and LSE of every
+ * key chunk).  chunk = 0 selects the built-in chunk size.  Returns 0 for
+ * invalid sizes.
+ */
+size_t fa_decode_workspace_size(int batch, int heads_q, int max_cache_len, int head_dim,
+                                int chunk);
+
+/*
+ * fa_fwd_decode_splitkv -- one query per sequence against a KV cache, with the
+ * keys split into chunks processed in parallel and merged by LSE weight
+ * (split-KV for a short query and long keys, "FlashAttention — IO 感知的精确
+ * 注意力 kernel", section 2.3 step 3 and the split-KV combine of section 7;
+ * the query-head group is folded into the row dimension, section 4).
+ *
+ *   q, o          : [batch, heads_q, head_dim]
+ *   k_cache, v_cache : [batch, max_cache_len, heads_kv, head_dim]
+ *   cache_seqlens : device int32 [batch]; sequence b uses cache rows
+ *                   [0, cache_seqlens[b]); values must lie in [0, max_cache_len]
+ *                   (read on the device, not validated there).  Rows past the
+ *                   length are never read.
+ *   lse           : [batch, heads_q]
+ *   chunk         : keys per split, a multiple of 128; 0 = built-in choice.
+ *   workspace     : device memory of at least
+ *                   fa_decode_workspace_size(batch, heads_q, max_cache_len,
+ *                   head_dim, chunk) bytes, 16-byte aligned; contents on entry
+ *                   are ignored, contents on return are unspecified.
+ *   heads_q / heads_kv must be <= 32.
+ * Enqueues the split kernel, then the combine, on `stream`.
+ */
+fa_status fa_fwd_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* cache_seqlens, void* o, float* lse,
+                                int batch, int heads_q, int heads_kv, int max_cache_len,
+                                int head_dim, float scale, int chunk,
+                                void* workspace, size_t workspace_bytes,
+                                fa_dtype o_dtype, void* stream);
+
+/*
+ * fa_combine -- LSE-weighted merge of partial results computed over disjoint
+ * key subsets (the block merge of the PKU lecture notes "FlashAttention",
+ * section 6, written with logsumexps):
+ *   M = max_s lse_part[r, s]
+ *   lse[r] = M + ln sum_s exp(lse_part[r, s] - M)
+ *   o[r, :] = sum_s exp(lse_part[r, s] - lse[r]) * o_part[r, s, :]
+ * A split with lse_part = -inf is empty and contributes nothing (its o_part
+ * values are not read).  All splits empty gives o = 0, lse = -inf.
+ *   o_part   : float32 [rows, n_splits, head_dim], each split's normalised O
+ *   lse_part : float32 [rows, n_splits]
+ *   o        : [rows, head_dim] in o_dtype;  lse : float32 [rows]
+ *   1 <= n_splits <= 4096.
+ */
+fa_status fa_combine(const float* o_part, const float* lse_part, int rows, int n_splits,
+                     int head_dim, void* o, float* lse, fa_dtype o_dtype, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* fa_status_string(fa_status status);
+
+/* Detail of the last non-FA_OK status returned on the calling thread
+ * (empty string if none).  Valid until the next call on that thread. */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

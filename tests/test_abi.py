@@ -1,0 +1,152 @@
+"""Host-only checks of the C ABI (no GPU needed, nothing is launched).
+
+The library loads, exports every function that include/fa.h declares, and
+rejects each invalid argument with its status code before any HIP call.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from exact_attention_84_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+OK, NULL, SHAPE, HEADDIM, GQA, DTYPE, ARCH, WORKSPACE, HIP, ARG = range(10)
+FAKE = 0x1000  # never dereferenced: validation rejects before any device work
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fa_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    for code, name in _lib.STATUS_NAMES.items():
+        assert lib.fa_status_string(code).decode() == name
+    assert lib.fa_status_string(77).decode() == "FA_ERR_UNKNOWN"
+
+
+def fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, batch=2, hq=8, hkv=2, nq=16, nk=16, d=128,
+             scale=0.088, causal=1, cuq=None, cuk=None, mq=0, mk=0, odt=0, stream=None)
+    a.update(kw)
+    return lib.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["batch"], a["hq"], a["hkv"],
+                      a["nq"], a["nk"], a["d"], a["scale"], a["causal"], a["cuq"], a["cuk"],
+                      a["mq"], a["mk"], a["odt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(o=None), NULL),
+    (dict(lse=None), NULL),
+    (dict(d=96), HEADDIM), (dict(d=256), HEADDIM), (dict(d=0), HEADDIM),
+    (dict(hq=0), SHAPE), (dict(hkv=0), SHAPE), (dict(batch=-1), SHAPE),
+    (dict(nq=-1), SHAPE), (dict(nk=-5), SHAPE),
+    (dict(hq=8, hkv=3), GQA),
+    (dict(scale=0.0), ARG), (dict(scale=-1.0), ARG), (dict(scale=float("inf")), ARG),
+    (dict(scale=float("nan")), ARG), (dict(causal=2), ARG),
+    (dict(odt=2), DTYPE), (dict(odt=-1), DTYPE),
+    (dict(cuq=FAKE, mq=-1, mk=10), SHAPE),
+])
+def test_fwd_rejects_before_launch(lib, kw, status):
+    assert fwd(lib, **kw) == status
+    assert lib.fa_last_error().decode()  # a detail message is set
+
+
+def test_fwd_empty_inputs_are_noops(lib):
+    # nothing to compute: returns FA_OK without touching a device
+    assert fwd(lib, batch=0) == OK
+    assert fwd(lib, nq=0) == OK
+    assert fwd(lib, cuq=FAKE, mq=0, mk=0) == OK
+
+
+def dec(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, o=FAKE, lse=FAKE, batch=4, hq=32, hkv=8,
+             ncache=4096, d=128, scale=0.088, chunk=0, ws=FAKE, wsb=1 << 40, odt=0, stream=None)
+    a.update(kw)
+    return lib.fa_fwd_decode_splitkv(a["q"], a["kc"], a["vc"], a["lens"], a["o"], a["lse"],
+                                     a["batch"], a["hq"], a["hkv"], a["ncache"], a["d"],
+                                     a["scale"], a["chunk"], a["ws"], a["wsb"], a["odt"],
+                                     a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULL), (dict(kc=None), NULL), (dict(vc=None), NULL), (dict(lens=None), NULL),
+    (dict(o=None), NULL), (dict(lse=None), NULL),
+    (dict(d=80), HEADDIM), (dict(hq=12, hkv=8), GQA), (dict(hq=0), SHAPE),
+    (dict(hq=64, hkv=1), SHAPE),  # group of 64 exceeds the 32-row fold
+    (dict(ncache=-1), SHAPE), (dict(scale=0.0), ARG), (dict(chunk=100), ARG),
+    (dict(chunk=-128), ARG), (dict(odt=3), DTYPE),
+    (dict(ws=None), WORKSPACE), (dict(wsb=16), WORKSPACE), (dict(ws=FAKE + 4), WORKSPACE),
+])
+def test_decode_rejects_before_launch(lib, kw, status):
+    assert dec(lib, **kw) == status
+
+
+def test_decode_workspace_size(lib):
+    ws = lib.fa_decode_workspace_size
+    # explicit chunk: rows * splits * (d + 1) floats
+    assert ws(64, 32, 32768, 128, 1024) == 64 * 32 * 32 * 129 * 4
+    assert ws(2, 4, 1000, 64, 256) == 2 * 4 * 4 * 65 * 4
+    assert ws(2, 4, 0, 64, 256) == 2 * 4 * 1 * 65 * 4
+    # default chunk never needs more than the explicit-chunk formula allows
+    for (b, h, n, d) in [(64, 32, 32768, 128), (1, 1, 100, 64), (3, 8, 5000, 128)]:
+        assert ws(b, h, n, d, 0) > 0
+    # invalid sizes give 0
+    assert ws(1, 1, 100, 96, 0) == 0
+    assert ws(1, 0, 100, 64, 0) == 0
+    assert ws(1, 1, 100, 64, 100) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(op=None), NULL), (dict(lp=None), NULL), (dict(o=None), NULL), (dict(lse=None), NULL),
+    (dict(d=32), HEADDIM), (dict(splits=0), SHAPE), (dict(splits=5000), SHAPE),
+    (dict(rows=-1), SHAPE), (dict(odt=9), DTYPE),
+])
+def test_combine_rejects_before_launch(lib, kw, status):
+    a = dict(op=FAKE, lp=FAKE, rows=10, splits=4, d=128, o=FAKE, lse=FAKE, odt=1, stream=None)
+    a.update(kw)
+    assert lib.fa_combine(a["op"], a["lp"], a["rows"], a["splits"], a["d"], a["o"], a["lse"],
+                          a["odt"], a["stream"]) == status
+
+
+def test_product_path_does_not_use_the_oracle():
+    """The HIP binding never imports the CPU oracle (no fallback path)."""
+    pkg = os.path.join(ROOT, "exact_attention_84_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), f
+                assert "oracle/" not in text, f
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    code = ("import os, sys; os.environ['FA_LIB_PATH']=sys.argv[1]\n"
+            "from exact_attention_84_amd import _lib\n"
+            "try:\n    _lib.load()\nexcept ImportError as e:\n    print('raised', e)\n")
+    r = subprocess.run(["python", "-c", code, str(tmp_path / "nope.so")], capture_output=True,
+                       text=True, cwd=ROOT)
+    assert "raised" in r.stdout and "no fallback" in r.stdout

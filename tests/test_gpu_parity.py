@@ -1,0 +1,226 @@
+"""Parity of the HIP path with the fp64 oracle, through the C ABI (needs a GPU).
+
+Small cases are compared element by element over the whole output; they span
+several tiles and end in ragged tails.  The full-size workloads are launched
+exactly as bench.py launches them and checked on sampled rows, which the
+oracle evaluates one by one from the definition.  Bound: max-abs 1e-2 on O
+(fp32 output; a bf16 output adds half a bf16 ulp of the exact value) and 1e-3
+on the natural-log LSE, no NaN or Inf.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from _gpu_helpers import check_lse, check_o, dev_bf16, dev_i32, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_attention_84_amd as fa
+    fa.load()
+    return fa
+
+
+def run_fixed(fa, q, k, v, causal, scale, out_dtype):
+    import torch
+    o, lse = fa.attention(dev_bf16(q), dev_bf16(k), dev_bf16(v), causal=causal, scale=scale,
+                          out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return host(o), host(lse)
+
+
+FIXED_CASES = [
+    # (B, Nq, Nk, Hq, Hkv, d, causal)
+    (2, 300, 300, 4, 2, 128, False),
+    (2, 300, 300, 4, 2, 128, True),
+    (1, 257, 257, 2, 2, 64, False),
+    (1, 257, 257, 2, 2, 64, True),
+    (2, 100, 333, 4, 1, 128, True),   # fewer queries than keys (bottom-right)
+    (1, 333, 100, 4, 4, 128, True),   # more queries than keys: early rows see nothing
+    (1, 1, 1, 1, 1, 128, True),
+    (3, 17, 17, 2, 1, 64, True),
+    (1, 129, 129, 8, 2, 128, False),
+    (1, 64, 700, 2, 2, 128, False),
+    (2, 200, 0, 2, 2, 64, False),     # no keys at all: O = 0, LSE = -inf
+]
+
+
+@pytest.mark.parametrize("case", FIXED_CASES, ids=[str(c) for c in FIXED_CASES])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_fixed_matches_oracle(fa, case, out):
+    import torch
+    bsz, nq, nk, hq, hkv, d, causal = case
+    say("fixed", case, out)
+    q, k, v = W.make_fixed(bsz, hq, hkv, nq, nk, d, seed=7, wid=101, k_mult=1.5)
+    scale = 1.0 / np.sqrt(d)
+    og, lg = run_fixed(fa, q, k, v, causal, scale,
+                       torch.float32 if out == "f32" else torch.bfloat16)
+    orf, lrf = oracle.attention(q, k, v, scale, causal)
+    check_o(og, orf, out == "bf16", str(case))
+    check_lse(lg, lrf, str(case))
+
+
+VARLEN_CASES = [
+    ([1, 17, 300, 0, 129, 64, 65], None, 4, 2, 128),
+    ([5, 250, 3, 77], [9, 300, 1, 77], 8, 2, 128),   # separate key lengths
+    ([130, 1, 64], None, 2, 1, 64),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=[str(c[0]) for c in VARLEN_CASES])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_matches_oracle(fa, case, causal):
+    import torch
+    lq, lk, hq, hkv, d = case
+    lk = lq if lk is None else lk
+    say("varlen", case, causal)
+    q, k, v, cu_q, cu_k = W.make_varlen(lq, lk, hq, hkv, d, seed=8, wid=102)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = fa.attention(dev_bf16(q), dev_bf16(k), dev_bf16(v), causal=causal, scale=scale,
+                          cu_seqlens_q=dev_i32(cu_q), cu_seqlens_k=dev_i32(cu_k),
+                          max_seqlen_q=max(lq), max_seqlen_k=max(lk), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    orf, lrf = oracle.attention_varlen(q, k, v, cu_q, cu_k, scale, causal)
+    check_o(host(o), orf, False, str(case))
+    check_lse(host(lse), lrf, str(case))
+
+
+DECODE_CASES = [
+    # (B, Hq, Hkv, Ncache, lengths, d, chunk)
+    (3, 8, 2, 1000, [1, 257, 1000], 128, 128),
+    (3, 8, 2, 1000, [1, 257, 1000], 128, 256),
+    (3, 8, 2, 1000, [1, 257, 1000], 128, 0),
+    (2, 32, 8, 3000, [2999, 0], 128, 512),
+    (4, 4, 4, 513, [513, 128, 129, 5], 64, 128),
+    (2, 32, 1, 700, [700, 33], 128, 384),   # MQA: 32 query heads on one KV head
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[str(c) for c in DECODE_CASES])
+def test_decode_matches_oracle(fa, case):
+    import torch
+    bsz, hq, hkv, ncache, lens, d, chunk = case
+    say("decode", case)
+    lens = np.array(lens, np.int32)
+    q, k, v = W.make_decode(bsz, hq, hkv, ncache, d, lens, seed=9, wid=103, tail="nan")
+    scale = 1.0 / np.sqrt(d)
+    o, lse = fa.decode(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_i32(lens), scale=scale,
+                       chunk=chunk, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    orf, lrf = oracle.decode(q, k, v, lens, scale)
+    check_o(host(o), orf, False, str(case))
+    check_lse(host(lse), lrf, str(case))
+
+
+def test_combine_matches_oracle_merge(fa):
+    import torch
+    say("combine")
+    rng = np.random.default_rng(10)
+    rows, splits, d = 37, 9, 128
+    o_part = rng.standard_normal((rows, splits, d)).astype(np.float32)
+    lse_part = (rng.standard_normal((rows, splits)) * 4).astype(np.float32)
+    lse_part[rng.random((rows, splits)) < 0.3] = -np.inf    # empty splits
+    lse_part[3] = -np.inf                                    # a row with no keys at all
+    o_part[np.isneginf(lse_part)] = np.nan                   # never read
+    og, lg = fa.combine(torch.from_numpy(o_part).cuda(), torch.from_numpy(lse_part).cuda())
+    torch.cuda.synchronize()
+    orf, lrf = oracle.merge_partials(o_part.astype(np.float64), lse_part.astype(np.float64))
+    assert np.abs(host(og) - orf).max() <= 1e-5
+    check_lse(host(lg), lrf)
+    assert np.all(host(og)[3] == 0)
+
+
+# --------------------------------------------------------------------------
+# full-size workloads, as timed by bench.py, on sampled rows
+# --------------------------------------------------------------------------
+def _sample_rows(rng, n, lengths, hq, causal):
+    rows = []
+    for _ in range(n):
+        b = int(rng.integers(len(lengths)))
+        L = int(lengths[b])
+        if L == 0:
+            continue
+        i = int(rng.choice([0, L - 1, int(rng.integers(L))]))
+        rows.append((b, i, int(rng.integers(hq))))
+    return rows
+
+
+@pytest.mark.parametrize("wid,causal", [(1, False), (2, False), (2, True), (3, True)])
+def test_full_workload_sampled_rows(fa, wid, causal):
+    import torch
+    w = W.WORKLOADS[wid]
+    say("workload", w.name, "causal" if causal else "full")
+    inp = W.make_workload(w, seed=0)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        o, lse = fa.attention(dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"]),
+                              causal=causal, scale=w.scale, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(11 + wid)
+        rows = _sample_rows(rng, 48, [w.seqlen_q] * w.batch, w.heads_q, causal)
+        if wid == 1:
+            rows = [(0, i, 0) for i in range(w.seqlen_q)]
+        orf, lrf = oracle.attention_rows(inp["q"], inp["k"], inp["v"], rows, w.scale, causal)
+        og = host(o)
+        lg = host(lse)
+        sel_o = np.stack([og[b, i, h] for (b, i, h) in rows])
+        sel_l = np.array([lg[b, i, h] for (b, i, h) in rows])
+        check_o(sel_o, orf, out_dtype == torch.bfloat16, w.name)
+        check_lse(sel_l, lrf, w.name)
+        assert np.isfinite(og).all() and np.isfinite(lg).all()
+
+
+def test_full_varlen_workload_sampled_rows(fa):
+    import torch
+    w = W.WORKLOADS[4]
+    say("workload", w.name)
+    inp = W.make_workload(w, seed=0)
+    cu = inp["cu_q"]
+    o, lse = fa.attention(dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"]),
+                          causal=True, scale=w.scale, cu_seqlens_q=dev_i32(cu),
+                          cu_seqlens_k=dev_i32(cu), max_seqlen_q=int(inp["lengths"].max()),
+                          max_seqlen_k=int(inp["lengths"].max()), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = _sample_rows(np.random.default_rng(15), 64, inp["lengths"], w.heads_q, True)
+    orf, lrf = oracle.attention_rows(inp["q"], inp["k"], inp["v"], rows, w.scale, True,
+                                     cu_q=cu, cu_k=cu)
+    og, lg = host(o), host(lse)
+    sel_o = np.stack([og[cu[b] + i, h] for (b, i, h) in rows])
+    sel_l = np.array([lg[cu[b] + i, h] for (b, i, h) in rows])
+    check_o(sel_o, orf, False, w.name)
+    check_lse(sel_l, lrf, w.name)
+    assert np.isfinite(og).all() and np.isfinite(lg).all()
+
+
+def test_full_decode_workload_sampled_sequences(fa):
+    import torch
+    w = W.WORKLOADS[5]
+    say("workload", w.name)
+    lens = W.workload_lengths(w, seed=0)
+    q = W.decode_q(w.batch, w.heads_q, w.head_dim, seed=0, wid=w.wid)
+    kc = torch.full((w.batch, w.seqlen_k, w.heads_kv, w.head_dim), float("nan"),
+                    dtype=torch.bfloat16, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    slices = {}
+    check_b = [0, int(np.argmax(lens)), int(np.argmin(lens)), w.batch - 1]
+    for b in range(w.batch):
+        kb, vb = W.decode_kv_slice(b, int(lens[b]), w.heads_kv, w.head_dim, seed=0, wid=w.wid)
+        kc[b, :lens[b]] = dev_bf16(kb)
+        vc[b, :lens[b]] = dev_bf16(vb)
+        if b in check_b:
+            slices[b] = (kb, vb)
+    o, lse = fa.decode(dev_bf16(q), kc, vc, dev_i32(lens), scale=w.scale,
+                       out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    og, lg = host(o), host(lse)
+    assert np.isfinite(og).all() and np.isfinite(lg).all()
+    for b in check_b:
+        kb, vb = slices[b]
+        orf, lrf = oracle.decode(q[b:b + 1], kb[None], vb[None], lens[b:b + 1], w.scale)
+        check_o(og[b], orf[0], False, f"{w.name} b={b}")
+        check_lse(lg[b], lrf[0], f"{w.name} b={b}")

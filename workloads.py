@@ -72,11 +72,12 @@ def _rng(seed: int, wid: int, tensor: int, slc: int = 0) -> np.random.Generator:
 
 
 def round_f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to bfloat16 (nearest, ties to even); return uint16 bits."""
+    """Round finite float32 values to bfloat16 (nearest, ties to even); return
+    uint16 bits.  (Only NaN payloads could wrap in the 32-bit add.)"""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    b = x.view(np.uint32).astype(np.uint64)
-    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
-    return b.astype(np.uint16)
+    b = x.view(np.uint32).copy()
+    b += np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))
+    return (b >> np.uint32(16)).astype(np.uint16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -135,22 +136,42 @@ def make_varlen(lengths_q, lengths_k, heads_q, heads_kv, head_dim, *, seed=0, wi
     return q, k, v, cu_q, cu_k
 
 
+BF16_NAN = np.uint16(0x7FC0)
+
+
+def decode_q(batch, heads_q, head_dim, *, seed=0, wid=0) -> np.ndarray:
+    """Decode queries q [B, Hq, d] (bf16 bits)."""
+    q = np.empty((batch, heads_q, head_dim), np.uint16)
+    for b in range(batch):
+        q[b] = normal_bf16(seed, wid, T_Q, (heads_q, head_dim), b)
+    return q
+
+
+def decode_kv_slice(b, n, heads_kv, head_dim, *, seed=0, wid=0):
+    """The n valid cache rows of sequence b: (k, v), each [n, Hkv, d] bf16 bits."""
+    return (normal_bf16(seed, wid, T_K, (n, heads_kv, head_dim), b),
+            normal_bf16(seed, wid, T_V, (n, heads_kv, head_dim), b))
+
+
 def make_decode(batch, heads_q, heads_kv, cache_len, head_dim, cache_seqlens, *, seed=0,
-                wid=0, tail="zero"):
+                wid=0, tail="zero", workers=8):
     """q [B,Hq,d]; k/v caches [B,cache_len,Hkv,d]; rows past cache_seqlens[b] are
     zero (tail="zero") or NaN (tail="nan", to show they are never used)."""
+    import concurrent.futures as cf
     cache_seqlens = np.asarray(cache_seqlens, np.int32)
-    q = np.empty((batch, heads_q, head_dim), np.uint16)
+    q = decode_q(batch, heads_q, head_dim, seed=seed, wid=wid)
     k = np.empty((batch, cache_len, heads_kv, head_dim), np.uint16)
     v = np.empty((batch, cache_len, heads_kv, head_dim), np.uint16)
-    fill = np.uint16(0x7FC0) if tail == "nan" else np.uint16(0)
-    for b in range(batch):
+    fill = BF16_NAN if tail == "nan" else np.uint16(0)
+
+    def one(b):
         n = int(cache_seqlens[b])
-        q[b] = normal_bf16(seed, wid, T_Q, (heads_q, head_dim), b)
-        k[b, :n] = normal_bf16(seed, wid, T_K, (n, heads_kv, head_dim), b)
-        v[b, :n] = normal_bf16(seed, wid, T_V, (n, heads_kv, head_dim), b)
+        k[b, :n], v[b, :n] = decode_kv_slice(b, n, heads_kv, head_dim, seed=seed, wid=wid)
         k[b, n:] = fill
         v[b, n:] = fill
+
+    with cf.ThreadPoolExecutor(max_workers=max(1, workers)) as ex:
+        list(ex.map(one, range(batch)))
     return q, k, v
 
 
