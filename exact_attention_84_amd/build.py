@@ -63,8 +63,20 @@ def build(jobs: int = 4, defines=(), out_lib: str = LIB, verbose: bool = False) 
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{r.stderr}")
+    _check_undefined(tmp)
     os.replace(tmp, out_lib)
     return out_lib
+
+
+def _check_undefined(lib: str) -> None:
+    """Refuse a library whose host side lacks a kernel launch stub (it would
+    only fail when loaded)."""
+    r = subprocess.run(["nm", "-D", "--undefined-only", lib], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in r.stdout.splitlines()
+               if "__device_stub__" in l or "_ZN2fa" in l]
+    if missing:
+        os.remove(lib)
+        raise RuntimeError("undefined symbols in the built library: " + ", ".join(missing))
 
 
 def main(argv=None):

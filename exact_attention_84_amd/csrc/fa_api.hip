@@ -105,7 +105,6 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  float scale, int causal, const int32_t* cu_seqlens_q,
                  const int32_t* cu_seqlens_k, int max_seqlen_q, int max_seqlen_k,
                  fa_dtype o_dtype, void* stream) {
-  if (!q || !k || !v || !o || !lse) return fail(FA_ERR_NULL, "q, k, v, o and lse must be non-NULL");
   if (!valid_head_dim(head_dim))
     return fail(FA_ERR_HEADDIM, "head_dim %d not supported (64 or 128)", head_dim);
   if (batch < 0 || heads_q <= 0 || heads_kv <= 0)
@@ -132,6 +131,15 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   if ((long long)batch * rows_q * heads_q * head_dim > kMaxElems ||
       (long long)batch * rows_k * heads_kv * head_dim > kMaxElems)
     return fail(FA_ERR_SHAPE, "tensor too large");
+  // Pointers are required only for tensors that will be touched: an empty
+  // tensor (no query rows, or no keys) may come with a NULL data pointer.
+  if (!q || !o || !lse) {
+    if ((long long)batch * rows_q > 0)
+      return fail(FA_ERR_NULL, "q, o and lse must be non-NULL");
+  }
+  if ((!k || !v) && (long long)batch * rows_k > 0)
+    return fail(FA_ERR_NULL, "k and v must be non-NULL");
+  if (varlen && !cu_seqlens_q) return fail(FA_ERR_NULL, "cu_seqlens_q is NULL");
   const int br = fa::fwd_block_rows(head_dim);
   const long long n_qtiles = (rows_q + br - 1) / br;
   const long long total = (long long)batch * heads_q * n_qtiles;

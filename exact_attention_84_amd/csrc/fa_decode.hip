@@ -189,6 +189,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (lane == 0) lse[row] = out_lse;
 }
 
+template __global__ void decode_kernel<128>(const DecodeParams);
+template __global__ void decode_kernel<64>(const DecodeParams);
+template __global__ void combine_kernel<128>(const float*, const float*, int, int, void*, float*,
+                                             int);
+template __global__ void combine_kernel<64>(const float*, const float*, int, int, void*, float*,
+                                            int);
+
 hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream) {
   if (head_dim == 128)
     hipLaunchKernelGGL(decode_kernel<128>, dim3(p.total), dim3(kDecodeWaves * 64), 0, stream, p);

@@ -54,10 +54,18 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
 }
 
 // Max / sum of a value across the two half-waves (lanes l and l ^ 32).
+// v_permlane32_swap(x, x) hands every lane both x[l % 32] and x[32 + l % 32],
+// so both halves get the identical result without an LDS round trip.
 __device__ __forceinline__ float halfwave_max(float x) {
-  return fmaxf(x, __shfl_xor(x, 32));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float halfwave_sum(float x) { return x + __shfl_xor(x, 32); }
+__device__ __forceinline__ float halfwave_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Key index (within a 32-key sub-tile) of accumulator element v of a lane in
 // half-wave hh, for the 32x32 MFMA output layout.
@@ -270,6 +278,143 @@ __device__ __forceinline__ void pv_subtile(WaveState<D, NT>& st, const uint16_t*
       for (int t = 0; t < NT; ++t) st.o[t][dt] = mfma_32x32x16(a, pb[t][u], st.o[t][dt]);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Row-major K and V tiles filled straight from global memory into LDS
+// (global_load_lds_dwordx4: each wave instruction writes 64 x 16 bytes of
+// consecutive LDS), with the 16-byte chunks of row r XOR-swizzled by sw(r).
+// sw keeps (a) the 8 consecutive rows of one K operand read and (b) the 4
+// rows x 2 chunks of one 16-lane transposing V read on distinct bank groups.
+// Rows past the end of the keys are loaded from the last valid row instead:
+// their scores are masked, so they only ever meet a zero probability.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int kv_swizzle(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+template <int D>
+__device__ __forceinline__ int kv_offset(int row, int chunk) {
+  return row * (2 * D) + ((chunk ^ kv_swizzle(row)) << 4);
+}
+
+template <int D, int BC, int NW>
+struct TileDMA {
+  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;        // rows per wave instruction
+  static constexpr int NI = BC / RPI;         // wave instructions per tile
+  static constexpr int PER_WAVE = NI / NW;
+  static_assert(NI % NW == 0, "tile rows must split evenly over the waves");
+
+  int row[PER_WAVE];  // tile row this lane fills in each of its instructions
+  int off[PER_WAVE];  // its element offset from the tile's first row
+
+  __device__ __forceinline__ void init(size_t row_stride, int wave, int lane) {
+    const int r_in = lane / CPR, pc = lane % CPR;
+#pragma unroll
+    for (int n = 0; n < PER_WAVE; ++n) {
+      row[n] = (wave + n * NW) * RPI + r_in;
+      off[n] = row[n] * (int)row_stride + ((pc ^ kv_swizzle(row[n])) << 3);
+    }
+  }
+
+  // Tile rows k0..k0+BC-1 of `base` into `lds`.  Rows past klast are read
+  // from row klast (their scores are masked later).
+  __device__ __forceinline__ void issue(const uint16_t* __restrict__ base, size_t row_stride,
+                                        int k0, int klast, char* lds, int wave, int lane) const {
+    const uint16_t* tile = base + (size_t)k0 * row_stride;
+    if (k0 + BC - 1 <= klast) {
+#pragma unroll
+      for (int n = 0; n < PER_WAVE; ++n)
+        __builtin_amdgcn_global_load_lds(tile + off[n],
+                                         (lds_void*)(lds + (wave + n * NW) * 1024), 16, 0, 0);
+    } else {
+      const int pc = lane % CPR;
+#pragma unroll
+      for (int n = 0; n < PER_WAVE; ++n) {
+        const int src = min(k0 + row[n], klast);
+        const uint16_t* g = base + (size_t)src * row_stride + ((pc ^ kv_swizzle(row[n])) << 3);
+        __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds + (wave + n * NW) * 1024), 16, 0,
+                                         0);
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// S^T sub-tiles kt = 0..NKT-1 (keys kt*32..) of a swizzled K tile, with the
+// independent accumulators interleaved so consecutive MFMAs do not depend on
+// each other.
+template <int D, int NT, int NKT>
+__device__ __forceinline__ void scores_tile(f32x16 (&s)[NKT][NT], const char* __restrict__ k_lds,
+                                            int kt0, const bf16x8 (&qf)[NT][D / 16], int m32,
+                                            int hh) {
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[kt][t][v] = 0.f;
+  // Fragments of step st+1 are read while step st's MFMAs run.
+  bf16x8 a[2][NKT];
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt)
+    a[0][kt] = *reinterpret_cast<const bf16x8*>(k_lds + kv_offset<D>((kt0 + kt) * 32 + m32, hh));
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    if (st + 1 < D / 16) {
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+        a[(st + 1) & 1][kt] = *reinterpret_cast<const bf16x8*>(
+            k_lds + kv_offset<D>((kt0 + kt) * 32 + m32, 2 * (st + 1) + hh));
+    }
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) s[kt][t] = mfma_32x32x16(a[st & 1][kt], qf[t][st], s[kt][t]);
+  }
+}
+
+// A operand of O^T = V^T P^T for head-dim rows dt*32.. and the 8 keys of a
+// lane's half-wave in the 16-key step (kt, u), read from a row-major V tile
+// with two transposing LDS reads.  ds_read_b64_tr_b16 transposes within each
+// group of 16 lanes: result lane i, element j is element i & 3 of the 8 bytes
+// addressed by source lane 4 j + (i >> 2).  Source lane k therefore points at
+// key row (k >> 2) and head-dim columns d0 + 4 (k & 3).. of the group's 4 keys.
+template <int D>
+__device__ __forceinline__ bf16x8 v_operand(const char* __restrict__ v_lds, int kt, int u, int dt,
+                                            int lane) {
+  const int k = lane & 15, q = lane >> 4;
+  const int hh = q >> 1, mh = q & 1;
+  const int col = dt * 32 + 16 * mh + 4 * (k & 3);  // head-dim element
+  const int chunk = col >> 3, half = (col & 4) << 1;  // 16-byte chunk, byte offset in it
+  const int row0 = kt * 32 + 16 * u + 4 * hh + (k >> 2);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(v_lds + kv_offset<D>(row0, chunk) + half));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(v_lds + kv_offset<D>(row0 + 8, chunk) + half));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// O^T += V^T P^T over NKT 32-key sub-tiles; the D/32 accumulators of a step
+// are independent and interleaved.
+template <int D, int NT, int NKT>
+__device__ __forceinline__ void pv_tile(WaveState<D, NT>& st, const char* __restrict__ v_lds,
+                                        int kt0, const bf16x8 (&pb)[NKT][NT][2], int lane) {
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const bf16x8 a = v_operand<D>(v_lds, kt0 + kt, u, dt, lane);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) st.o[t][dt] = mfma_32x32x16(a, pb[kt][t][u], st.o[t][dt]);
+      }
 }
 
 }  // namespace fa

@@ -21,12 +21,13 @@ template <int D, int NW, int NT, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
 void fwd_kernel(const FwdParams p) {
   constexpr int BC = 64;
-  constexpr int T = NW * 64;
   constexpr int BR = NW * 32 * NT;
-  using Loader = TileLoader<D, BC, T>;
-  constexpr int KSTR = Loader::KSTR;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[Loader::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[Loader::VT_ELEMS];
+  constexpr int TILE_BYTES = BC * D * 2;
+  // Two stages of K and V: the next tile streams in while this one is used.
+  __shared__ __attribute__((aligned(1024))) char k_lds0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -74,6 +75,13 @@ void fwd_kernel(const FwdParams p) {
   const uint16_t* kbase = p.k + (size_t)k_start * kv_stride + (size_t)kvh * D;
   const uint16_t* vbase = p.v + (size_t)k_start * kv_stride + (size_t)kvh * D;
 
+  TileDMA<D, BC, NW> dma;
+  dma.init(kv_stride, wave, lane);
+  if (n_kt > 0) {
+    dma.issue(kbase, kv_stride, 0, Lk - 1, k_lds0, wave, lane);
+    dma.issue(vbase, kv_stride, 0, Lk - 1, v_lds0, wave, lane);
+  }
+
   WaveState<D, NT> st;
   st.init();
 #pragma unroll
@@ -88,21 +96,20 @@ void fwd_kernel(const FwdParams p) {
     }
   }
 
-  Loader ld;
-  if (n_kt > 0) ld.load(kbase, vbase, kv_stride, 0, Lk, tid);
-
   for (int j = 0; j < n_kt; ++j) {
     const int k0 = j * BC;
-    __syncthreads();  // every wave is done reading the previous tile
-    ld.store(k_lds, vt_lds, tid);
-    __syncthreads();
-    if (j + 1 < n_kt) ld.load(kbase, vbase, kv_stride, k0 + BC, Lk, tid);
+    wait_dma();       // this wave's share of tile j has landed in LDS
+    __syncthreads();  // everyone's share has; everyone is done with tile j-1
+    const char* k_cur = (j & 1) ? k_lds1 : k_lds0;
+    const char* v_cur = (j & 1) ? v_lds1 : v_lds0;
+    if (j + 1 < n_kt) {
+      dma.issue(kbase, kv_stride, k0 + BC, Lk - 1, (j & 1) ? k_lds0 : k_lds1, wave, lane);
+      dma.issue(vbase, kv_stride, k0 + BC, Lk - 1, (j & 1) ? v_lds0 : v_lds1, wave, lane);
+    }
 
     if (wave_active && k0 <= wave_last_key) {
       f32x16 s[BC / 32][NT];
-#pragma unroll
-      for (int kt = 0; kt < BC / 32; ++kt)
-        scores_subtile<D, NT, KSTR>(s[kt], k_lds, kt, st.qf, m32, hh);
+      scores_tile<D, NT, BC / 32>(s, k_cur, 0, st.qf, m32, hh);
 
       const bool edge = (k0 + BC > Lk) || (CAUSAL && k0 + BC - 1 > qw0 + delta);
       if (edge) {
@@ -122,8 +129,7 @@ void fwd_kernel(const FwdParams p) {
 
       bf16x8 pb[BC / 32][NT][2];
       softmax_update<D, NT, BC / 32>(st, s, pb, p.c);
-#pragma unroll
-      for (int kt = 0; kt < BC / 32; ++kt) pv_subtile<D, NT, BC>(st, vt_lds, kt, pb[kt], m32, hh);
+      pv_tile<D, NT, BC / 32>(st, v_cur, 0, pb, lane);
     }
   }
 
@@ -161,6 +167,13 @@ void fwd_kernel(const FwdParams p) {
     }
   }
 }
+
+// Explicit instantiations: every kernel the dispatcher can launch is emitted
+// on both the device and the host side.
+template __global__ void fwd_kernel<128, kFwdWaves, kFwdNT, false>(const FwdParams);
+template __global__ void fwd_kernel<128, kFwdWaves, kFwdNT, true>(const FwdParams);
+template __global__ void fwd_kernel<64, kFwdWaves, kFwdNT, false>(const FwdParams);
+template __global__ void fwd_kernel<64, kFwdWaves, kFwdNT, true>(const FwdParams);
 
 template <int D, int NW, int NT, bool CAUSAL>
 static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {

@@ -76,10 +76,22 @@ def test_fwd_rejects_before_launch(lib, kw, status):
 
 
 def test_fwd_empty_inputs_are_noops(lib):
-    # nothing to compute: returns FA_OK without touching a device
+    # nothing to compute: returns FA_OK without touching a device, and empty
+    # tensors may have NULL data pointers
     assert fwd(lib, batch=0) == OK
     assert fwd(lib, nq=0) == OK
+    assert fwd(lib, nq=0, q=None, o=None, lse=None) == OK
+    assert fwd(lib, batch=0, q=None, k=None, v=None, o=None, lse=None) == OK
     assert fwd(lib, cuq=FAKE, mq=0, mk=0) == OK
+
+
+def test_fwd_null_keys_rejected_when_keys_exist(lib):
+    # k / v may be NULL only when there are no keys; every call here stops in
+    # validation (none reaches a device)
+    assert fwd(lib, nk=4, k=None) == NULL
+    assert fwd(lib, nk=4, v=None) == NULL
+    assert fwd(lib, cuq=FAKE, mq=4, mk=4, k=None) == NULL
+    assert fwd(lib, nk=0, k=None, v=None, batch=0) == OK
 
 
 def dec(lib, **kw):

@@ -52,6 +52,9 @@ def test_equal_scores_give_prefix_means(fa, wid):
 
 
 def test_constant_v_gives_constant_o(fa):
+    """O = c exactly in the definition; the kernel multiplies bf16-rounded
+    probabilities with V but divides by the fp32 sum, so it is off by at most
+    2^-9 |c| (the relative rounding bound of bf16) from c."""
     import torch
     w = W.WORKLOADS[2]
     say("constant V")
@@ -61,7 +64,7 @@ def test_constant_v_gives_constant_o(fa):
     for causal in (False, True):
         o, _ = fa.attention(dev_bf16(inp["q"]), dev_bf16(inp["k"]), v, causal=causal,
                             scale=w.scale, out_dtype=torch.float32)
-        assert (o + 2.5).abs().max().item() <= 1e-5
+        assert (o + 2.5).abs().max().item() <= 2.5 * 2.0 ** -9
 
 
 def test_causal_row_zero_is_v0(fa):
