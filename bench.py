@@ -150,6 +150,27 @@ def other_workloads(fa, steps, warmup):
     return res
 
 
+def probe(fa, w, steps, warmup):
+    """Launches for rocprofv3 counter runs: the headline workload's non-causal
+    and causal forward, then a 1 GiB device-to-device copy (a kernel that reads
+    and writes exactly 1 GiB each, to scale the byte counters)."""
+    import torch
+    inp = W.make_workload(w, seed=0)
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+    for causal in (False, True):
+        for _ in range(warmup + steps):
+            fa.attention(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse)
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"probe: {warmup + steps} non-causal, {warmup + steps} causal launches, "
+        f"{steps} copies of {a.numel() * 4} bytes")
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The fp64 oracle on (sequence, head) slices of the workload, both modes,
     until the time budget is spent."""
@@ -185,6 +206,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--probe", action="store_true",
+                    help="counter-collection mode: only the timed launches of the headline "
+                         "workload plus a plain 1 GiB device copy (the scale for HBM byte "
+                         "counters); prints no JSON")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
@@ -202,6 +227,9 @@ def main():
         props.multi_processor_count)
 
     w = W.WORKLOADS[2]
+    if a.probe:
+        probe(fa, w, a.steps, a.warmup)
+        return
     inp = W.make_workload(w, seed=0)
     q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
     o_nc, o_c = torch.empty_like(q), torch.empty_like(q)

@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_layout.hpp"
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -218,11 +220,27 @@ __device__ __forceinline__ void scores_subtile(f32x16 (&s)[NT], const uint16_t* 
   }
 }
 
-// Online-softmax update for NKT score sub-tiles: new running max, rescale
-// factor, probabilities (fp32 for the row sum, bf16 for the P V product).
+// Lazy rescaling threshold, in log2 units.  The online-softmax result is exact
+// for any per-row reference value r in place of the running max, as long as
+// exp2(s c - r) cannot overflow: O and l are both accumulated relative to r,
+// and LSE = ln2 (r + log2 l).  The reference is moved to the new maximum (and
+// O, l rescaled by 2^(r_old - r_new)) only when a row's maximum exceeds it by
+// more than kRescaleTau, so probabilities stay below 2^kRescaleTau and most
+// tiles skip the O rescale altogether.  kRescaleTau = 0 moves it on every
+// increase, which is the rescale-only-when-the-max-grows rule.
+#ifndef FA_RESCALE_TAU
+#define FA_RESCALE_TAU 8.0f
+#endif
+constexpr float kRescaleTau = FA_RESCALE_TAU;
+
+// Online-softmax probabilities for NKT score sub-tiles: new reference, the
+// rescale factor alpha, probabilities (fp32 for the row sum, bf16 for the P V
+// product).  Returns whether any row of the wave moved its reference.
 template <int D, int NT, int NKT>
-__device__ __forceinline__ void softmax_update(WaveState<D, NT>& st, f32x16 (&s)[NKT][NT],
-                                               bf16x8 (&pb)[NKT][NT][2], float c) {
+__device__ __forceinline__ bool softmax_probs(WaveState<D, NT>& st, f32x16 (&s)[NKT][NT],
+                                              bf16x8 (&pb)[NKT][NT][2], float (&alpha)[NT],
+                                              float c) {
+  bool moved = false;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     float mx = -INFINITY;
@@ -230,36 +248,50 @@ __device__ __forceinline__ void softmax_update(WaveState<D, NT>& st, f32x16 (&s)
     for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt][t][v]);
-    mx = halfwave_max(mx);
-    const float mnew = fmaxf(st.mc[t], mx * c);
-    // A row that has seen only masked keys keeps m = -inf; subtract 0 then so
+    const float mx_c = halfwave_max(mx) * c;
+    const float mref = (mx_c > st.mc[t] + kRescaleTau) ? mx_c : st.mc[t];
+    moved |= mref != st.mc[t];
+    // A row that has seen only masked keys keeps r = -inf; subtract 0 then so
     // that exp2(-inf - 0) = 0 instead of NaN.
-    const float msub = (mnew == -INFINITY) ? 0.f : mnew;
-    const float alpha = fast_exp2(st.mc[t] - msub);
+    const float msub = (mref == -INFINITY) ? 0.f : mref;
+    alpha[t] = fast_exp2(st.mc[t] - msub);
     float rs = 0.f;
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        float p[8];
+        float pr[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          p[e] = fast_exp2(fmaf(s[kt][t][8 * u + e], c, -msub));
-          rs += p[e];
+          pr[e] = fast_exp2(fmaf(s[kt][t][8 * u + e], c, -msub));
+          rs += pr[e];
         }
-        pb[kt][t][u] = pack_bf16x8(p);
+        pb[kt][t][u] = pack_bf16x8(pr);
       }
-    st.l[t] = alpha * st.l[t] + rs;
-    st.mc[t] = mnew;
-    // Rescale the accumulator only when some row's max moved (alpha != 1);
-    // skipping alpha == 1 is exact.
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) st.o[t][dt][v] *= alpha;
-    }
+    st.l[t] = fmaf(alpha[t], st.l[t], rs);
+    st.mc[t] = mref;
   }
+  return moved;
+}
+
+template <int D, int NT>
+__device__ __forceinline__ void rescale_o(WaveState<D, NT>& st, const float (&alpha)[NT]) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) st.o[t][dt][v] *= alpha[t];
+}
+
+// Probabilities plus the O rescale, skipped (exactly) when no row of the wave
+// moved its reference.
+template <int D, int NT, int NKT>
+__device__ __forceinline__ void softmax_update(WaveState<D, NT>& st, f32x16 (&s)[NKT][NT],
+                                               bf16x8 (&pb)[NKT][NT][2], float c) {
+  float alpha[NT];
+  const bool moved = softmax_probs<D, NT, NKT>(st, s, pb, alpha, c);
+  if (__any(moved)) rescale_o<D, NT>(st, alpha);
 }
 
 // O^T += V^T P^T for keys kt*32..kt*32+31 of the LDS V^T tile (row stride BC).
@@ -284,20 +316,15 @@ __device__ __forceinline__ void pv_subtile(WaveState<D, NT>& st, const uint16_t*
 // Row-major K and V tiles filled straight from global memory into LDS
 // (global_load_lds_dwordx4: each wave instruction writes 64 x 16 bytes of
 // consecutive LDS), with the 16-byte chunks of row r XOR-swizzled by sw(r).
-// sw keeps (a) the 8 consecutive rows of one K operand read and (b) the 4
-// rows x 2 chunks of one 16-lane transposing V read on distinct bank groups.
+// gfx950's LDS has 64 banks of 4 bytes (256 bytes per clock): a 16-byte read
+// serves 16 lanes per clock, an 8-byte read 32.  sw puts on distinct bank
+// groups (a) the 16 consecutive rows of one K operand read (same chunk) and
+// (b) the 4 rows x 4 chunks of the 32 lanes of one transposing V read.
 // Rows past the end of the keys are loaded from the last valid row instead:
 // their scores are masked, so they only ever meet a zero probability.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ int kv_swizzle(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-
-template <int D>
-__device__ __forceinline__ int kv_offset(int row, int chunk) {
-  return row * (2 * D) + ((chunk ^ kv_swizzle(row)) << 4);
-}
 
 template <int D, int BC, int NW>
 struct TileDMA {
@@ -307,15 +334,18 @@ struct TileDMA {
   static constexpr int PER_WAVE = NI / NW;
   static_assert(NI % NW == 0, "tile rows must split evenly over the waves");
 
-  int row[PER_WAVE];  // tile row this lane fills in each of its instructions
-  int off[PER_WAVE];  // its element offset from the tile's first row
+  int off[PER_WAVE];  // element offset, from the tile's first row, of the
+                      // chunk this lane fills in each of its instructions
+
+  __device__ __forceinline__ static int row_of(int n, int wave, int lane) {
+    return dma_row<D>(wave + n * NW, lane);
+  }
 
   __device__ __forceinline__ void init(size_t row_stride, int wave, int lane) {
-    const int r_in = lane / CPR, pc = lane % CPR;
 #pragma unroll
     for (int n = 0; n < PER_WAVE; ++n) {
-      row[n] = (wave + n * NW) * RPI + r_in;
-      off[n] = row[n] * (int)row_stride + ((pc ^ kv_swizzle(row[n])) << 3);
+      const int row = row_of(n, wave, lane);
+      off[n] = row * (int)row_stride + (dma_chunk<D>(wave + n * NW, lane) << 3);
     }
   }
 
@@ -330,11 +360,12 @@ struct TileDMA {
         __builtin_amdgcn_global_load_lds(tile + off[n],
                                          (lds_void*)(lds + (wave + n * NW) * 1024), 16, 0, 0);
     } else {
-      const int pc = lane % CPR;
 #pragma unroll
       for (int n = 0; n < PER_WAVE; ++n) {
-        const int src = min(k0 + row[n], klast);
-        const uint16_t* g = base + (size_t)src * row_stride + ((pc ^ kv_swizzle(row[n])) << 3);
+        const int row = row_of(n, wave, lane);
+        const int src = min(k0 + row, klast);
+        const uint16_t* g =
+            base + (size_t)src * row_stride + (dma_chunk<D>(wave + n * NW, lane) << 3);
         __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds + (wave + n * NW) * 1024), 16, 0,
                                          0);
       }
@@ -342,76 +373,93 @@ struct TileDMA {
   }
 };
 
+// Per-lane LDS byte offsets of the MFMA operand reads from swizzled K / V
+// tiles: one base register per head-dim step plus compile-time offsets for
+// the key sub-tile (the swizzle depends only on the low row bits, which the
+// lane fixes).
+template <int D>
+struct LdsRead {
+  static constexpr int KS = D / 16;  // score k-steps
+  static constexpr int DT = D / 32;  // head-dim blocks of the P V product
+  uint32_t kb[KS];                   // K operand of score k-step st, keys 0..31
+  uint32_t vb[DT][2];                // V operand of block dt, key rows +0 / +8
+
+  __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+    for (int st = 0; st < KS; ++st) kb[st] = k_read_offset<D>(lane, st);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int sec = 0; sec < 2; ++sec) vb[dt][sec] = v_read_offset<D>(lane, dt, sec);
+  }
+
+  // A operand of S^T = K Q^T: keys kt*32.., head-dim step st.  Key rows
+  // kt*32 + m32 share the swizzle of m32.
+  __device__ __forceinline__ bf16x8 k(const char* __restrict__ lds, int kt, int st) const {
+    return *reinterpret_cast<const bf16x8*>(lds + kb[st] + kt * 64 * D);
+  }
+
+  // A operand of O^T = V^T P^T for head-dim rows dt*32.. and the 8 keys of
+  // the lane's half-wave in the 16-key step (kt, u), from a row-major V tile,
+  // with two transposing LDS reads.  ds_read_b64_tr_b16 transposes within
+  // each group of 16 lanes: result lane i, element j is element i & 3 of the
+  // 8 bytes addressed by source lane 4 j + (i >> 2).  Rows kt*32 + 16 u + r
+  // share the swizzle of r.
+  __device__ __forceinline__ bf16x8 v(const char* __restrict__ lds, int kt, int u, int dt) const {
+    const char* a = lds + (kt * 32 + 16 * u) * 2 * D;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(a + vb[dt][0]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(a + vb[dt][1]));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, w);
+  }
+};
+
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 
 // S^T sub-tiles kt = 0..NKT-1 (keys kt*32..) of a swizzled K tile, with the
 // independent accumulators interleaved so consecutive MFMAs do not depend on
-// each other.
-template <int D, int NT, int NKT>
+// each other; the fragments of step st+1 are read while step st's MFMAs run.
+template <int D, int NT, int NKT, bool PREFETCH = true>
 __device__ __forceinline__ void scores_tile(f32x16 (&s)[NKT][NT], const char* __restrict__ k_lds,
-                                            int kt0, const bf16x8 (&qf)[NT][D / 16], int m32,
-                                            int hh) {
-#pragma unroll
-  for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[kt][t][v] = 0.f;
-  // Fragments of step st+1 are read while step st's MFMAs run.
+                                            const LdsRead<D>& rd,
+                                            const bf16x8 (&qf)[NT][D / 16]) {
   bf16x8 a[2][NKT];
 #pragma unroll
-  for (int kt = 0; kt < NKT; ++kt)
-    a[0][kt] = *reinterpret_cast<const bf16x8*>(k_lds + kv_offset<D>((kt0 + kt) * 32 + m32, hh));
+  for (int kt = 0; kt < NKT; ++kt) a[0][kt] = rd.k(k_lds, kt, 0);
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) {
-    if (st + 1 < D / 16) {
+    if (!PREFETCH && st > 0) {
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-        a[(st + 1) & 1][kt] = *reinterpret_cast<const bf16x8*>(
-            k_lds + kv_offset<D>((kt0 + kt) * 32 + m32, 2 * (st + 1) + hh));
+      for (int kt = 0; kt < NKT; ++kt) a[st & 1][kt] = rd.k(k_lds, kt, st);
+    }
+    if (PREFETCH && st + 1 < D / 16) {
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) a[(st + 1) & 1][kt] = rd.k(k_lds, kt, st + 1);
     }
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) s[kt][t] = mfma_32x32x16(a[st & 1][kt], qf[t][st], s[kt][t]);
+      for (int t = 0; t < NT; ++t)
+        s[kt][t] = mfma_32x32x16(a[st & 1][kt], qf[t][st], st == 0 ? f32x16{} : s[kt][t]);
   }
-}
-
-// A operand of O^T = V^T P^T for head-dim rows dt*32.. and the 8 keys of a
-// lane's half-wave in the 16-key step (kt, u), read from a row-major V tile
-// with two transposing LDS reads.  ds_read_b64_tr_b16 transposes within each
-// group of 16 lanes: result lane i, element j is element i & 3 of the 8 bytes
-// addressed by source lane 4 j + (i >> 2).  Source lane k therefore points at
-// key row (k >> 2) and head-dim columns d0 + 4 (k & 3).. of the group's 4 keys.
-template <int D>
-__device__ __forceinline__ bf16x8 v_operand(const char* __restrict__ v_lds, int kt, int u, int dt,
-                                            int lane) {
-  const int k = lane & 15, q = lane >> 4;
-  const int hh = q >> 1, mh = q & 1;
-  const int col = dt * 32 + 16 * mh + 4 * (k & 3);  // head-dim element
-  const int chunk = col >> 3, half = (col & 4) << 1;  // 16-byte chunk, byte offset in it
-  const int row0 = kt * 32 + 16 * u + 4 * hh + (k >> 2);
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(v_lds + kv_offset<D>(row0, chunk) + half));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(v_lds + kv_offset<D>(row0 + 8, chunk) + half));
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, w);
 }
 
 // O^T += V^T P^T over NKT 32-key sub-tiles; the D/32 accumulators of a step
 // are independent and interleaved.
 template <int D, int NT, int NKT>
 __device__ __forceinline__ void pv_tile(WaveState<D, NT>& st, const char* __restrict__ v_lds,
-                                        int kt0, const bf16x8 (&pb)[NKT][NT][2], int lane) {
+                                        const LdsRead<D>& rd, const bf16x8 (&pb)[NKT][NT][2]) {
 #pragma unroll
   for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const bf16x8 a = v_operand<D>(v_lds, kt0 + kt, u, dt, lane);
+        const bf16x8 a = rd.v(v_lds, kt, u, dt);
 #pragma unroll
         for (int t = 0; t < NT; ++t) st.o[t][dt] = mfma_32x32x16(a, pb[kt][t][u], st.o[t][dt]);
       }

@@ -10,10 +10,115 @@
 // FlashAttention 1-4 详解", section FlashAttention 2 的工程优化, causal
 // lower-triangle skipping).  Masks are applied only on tiles that cross the
 // diagonal or the end of the keys.
+//
+// Within a wave the key loop is software-pipelined so that the matrix core and
+// the ALUs work at the same time (the GEMM/softmax overlap of the first page's
+// FlashAttention 3 notes, section FlashAttention 3 的硬件特性利用, done here
+// inside one wavefront): step j issues the score MFMAs of tile j+1 and the
+// P V MFMAs of tile j-1, and runs the softmax of tile j between them.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
 namespace fa {
+
+// One steady-state step of a wave owning NT groups of 32 query rows, 64-key
+// tiles:
+//   s      = Q K_j^T            (D/8 K fragments, NT MFMAs each)
+//   O     += P_{j-1} V_{j-1}    (D/8 V fragments, NT MFMAs each)
+//   softmax of s (tile j) -> pout, alpha
+// The P V MFMAs do not depend on the new scores, so each of them is followed
+// by a slice of the softmax of s (sched_barrier fences keep that order): the
+// wave keeps issuing ALU instructions while the matrix core works.  Returns
+// whether a row moved its reference (alpha then holds the rescale factors).
+template <int D, int NT>
+__device__ __forceinline__ bool steady_step(WaveState<D, NT>& st, const char* __restrict__ k_cur,
+                                            const char* __restrict__ v_prev, const LdsRead<D>& rd,
+                                            const bf16x8 (&pin)[2][NT][2],
+                                            bf16x8 (&pout)[2][NT][2], float (&alpha)[NT],
+                                            float c) {
+  constexpr int DT = D / 32;
+  constexpr int SLOTS = D / 8;                  // V fragments per step
+  constexpr int LEAD = 2;                       // P V MFMAs before the first slice
+  constexpr int NE = 32 * NT;                   // probabilities per lane
+  constexpr int EXP_SLOTS = SLOTS - LEAD - 2;   // two slots hold the row maxima
+  constexpr int PER = (NE + EXP_SLOTS - 1) / EXP_SLOTS;
+  static_assert(4 * DT == SLOTS, "slot bookkeeping");
+
+  f32x16 s[2][NT];
+  scores_tile<D, NT, 2>(s, k_cur, rd, st.qf);
+
+  float mx[NT], msub[NT], rs[NT], mref[NT];
+  uint32_t pk[NT][16];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    mx[t] = -INFINITY;
+    rs[t] = 0.f;
+  }
+  bf16x8 va = rd.v(v_prev, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) {
+    const int pkt = i / (2 * DT), pu = (i / DT) & 1, pdt = i % DT;
+    const bf16x8 vcur = va;
+    if (i + 1 < SLOTS) {
+      const int n = i + 1;
+      va = rd.v(v_prev, n / (2 * DT), (n / DT) & 1, n % DT);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      st.o[t][pdt] = mfma_32x32x16(vcur, pin[pkt][t][pu], st.o[t][pdt]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i == LEAD) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx[t] = fmaxf(mx[t], s[0][t][v]);
+    } else if (i == LEAD + 1) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx[t] = fmaxf(mx[t], s[1][t][v]);
+        const float mx_c = halfwave_max(mx[t]) * c;
+        mref[t] = (mx_c > st.mc[t] + kRescaleTau) ? mx_c : st.mc[t];
+        msub[t] = (mref[t] == -INFINITY) ? 0.f : mref[t];
+        alpha[t] = fast_exp2(st.mc[t] - msub[t]);
+      }
+    } else if (i > LEAD + 1) {
+      const int e0 = (i - LEAD - 2) * PER;
+#pragma unroll
+      for (int g = e0; g < e0 + PER && g < NE; ++g) {
+        const int t = g >> 5, e = g & 31;
+        const float pe = fast_exp2(fmaf(s[e >> 4][t][e & 15], c, -msub[t]));
+        s[e >> 4][t][e & 15] = pe;
+        rs[t] += pe;
+        if (e & 1) {
+          pk[t][e >> 1] = pack_bf16x2(s[e >> 4][t][(e - 1) & 15], pe);
+          // keep the conversion in this slice (it would otherwise sink to
+          // its use in the next step)
+          asm volatile("" ::"v"(pk[t][e >> 1]));
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(rs[t]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  bool moved = false;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const u32x4 w = {pk[t][8 * kt + 4 * u], pk[t][8 * kt + 4 * u + 1],
+                         pk[t][8 * kt + 4 * u + 2], pk[t][8 * kt + 4 * u + 3]};
+        pout[kt][t][u] = __builtin_bit_cast(bf16x8, w);
+      }
+    st.l[t] = fmaf(alpha[t], st.l[t], rs[t]);
+    moved |= mref[t] != st.mc[t];
+    st.mc[t] = mref[t];
+  }
+  return moved;
+}
 
 // Two waves per SIMD (256 registers each) when a wave owns 32 query rows, so
 // that one wave's MFMAs overlap the other's softmax arithmetic.
@@ -21,16 +126,21 @@ template <int D, int NW, int NT, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
 void fwd_kernel(const FwdParams p) {
   constexpr int BC = 64;
+  constexpr int NKT = BC / 32;
   constexpr int BR = NW * 32 * NT;
   constexpr int TILE_BYTES = BC * D * 2;
-  // Two stages of K and V: the next tile streams in while this one is used.
+  // Two stages of K and V: the next tiles stream in while these are used.
   __shared__ __attribute__((aligned(1024))) char k_lds0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char k_lds1[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v_lds0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v_lds1[TILE_BYTES];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  // The wave index is the same for all lanes; saying so keeps every quantity
+  // derived from it (this wave's rows, its tile count, the loop conditions) in
+  // scalar registers and the control flow wave-uniform.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m32 = lane & 31, hh = lane >> 5;
 
   // ---- work item: (sequence b, kv head, query head in group, query tile) ----
@@ -69,6 +179,8 @@ void fwd_kernel(const FwdParams p) {
   const int qw0 = q0 + wave * 32 * NT;
   const bool wave_active = qw0 < Lq;
   const int wave_last_key = CAUSAL ? min(Lk - 1, qw0 + 32 * NT - 1 + delta) : Lk - 1;
+  // Key tiles this wave needs (causal: up to its own diagonal).
+  const int wn = (wave_active && wave_last_key >= 0) ? min(n_kt, wave_last_key / BC + 1) : 0;
 
   const size_t q_stride = (size_t)p.hq * D;
   const size_t kv_stride = (size_t)p.hkv * D;
@@ -77,10 +189,9 @@ void fwd_kernel(const FwdParams p) {
 
   TileDMA<D, BC, NW> dma;
   dma.init(kv_stride, wave, lane);
-  if (n_kt > 0) {
-    dma.issue(kbase, kv_stride, 0, Lk - 1, k_lds0, wave, lane);
-    dma.issue(vbase, kv_stride, 0, Lk - 1, v_lds0, wave, lane);
-  }
+  LdsRead<D> rd;
+  rd.init(lane);
+  if (n_kt > 0) dma.issue(kbase, kv_stride, 0, Lk - 1, k_lds0, wave, lane);
 
   WaveState<D, NT> st;
   st.init();
@@ -96,44 +207,102 @@ void fwd_kernel(const FwdParams p) {
     }
   }
 
-  for (int j = 0; j < n_kt; ++j) {
+  // Score tile j needs a mask when it crosses the end of the keys or (causal)
+  // this wave's diagonal; both only grow with j.
+  auto edge_tile = [&](int j) {
     const int k0 = j * BC;
-    wait_dma();       // this wave's share of tile j has landed in LDS
-    __syncthreads();  // everyone's share has; everyone is done with tile j-1
+    return (k0 + BC > Lk) || (CAUSAL && k0 + BC - 1 > qw0 + delta);
+  };
+  // Step j: K_j and V_{j-1} are in LDS; K_{j+1} and V_j start streaming into
+  // the stages that K_{j-1} and V_{j-2} used.
+  auto stage = [&](int j) {
+    wait_dma();       // this wave's share of K_j and V_{j-1} has landed
+    __syncthreads();  // everyone's has, and everyone is done with K_{j-1}, V_{j-2}
+    if (j + 1 < n_kt)
+      dma.issue(kbase, kv_stride, (j + 1) * BC, Lk - 1, (j & 1) ? k_lds0 : k_lds1, wave, lane);
+    if (j < n_kt)
+      dma.issue(vbase, kv_stride, j * BC, Lk - 1, (j & 1) ? v_lds1 : v_lds0, wave, lane);
+  };
+
+  // The O rescale of tile j (alpha_j, when some row moved its reference) must
+  // land after P_{j-1} V_{j-1} and before P_j V_j: it is applied at the top of
+  // step j+1.  p_a / p_b hold the probabilities of tiles j-1 and j.
+  bf16x8 p_a[NKT][NT][2], p_b[NKT][NT][2];
+  float alpha[NT];
+  bool moved = false;
+
+  // One step done phase by phase (first tile, masked tiles, the final P V).
+  auto general_step = [&](int j) {
+    stage(j);
     const char* k_cur = (j & 1) ? k_lds1 : k_lds0;
-    const char* v_cur = (j & 1) ? v_lds1 : v_lds0;
-    if (j + 1 < n_kt) {
-      dma.issue(kbase, kv_stride, k0 + BC, Lk - 1, (j & 1) ? k_lds0 : k_lds1, wave, lane);
-      dma.issue(vbase, kv_stride, k0 + BC, Lk - 1, (j & 1) ? v_lds0 : v_lds1, wave, lane);
+    const char* v_prev = (j & 1) ? v_lds0 : v_lds1;
+    if (j >= 1 && j <= wn) {
+      if (__any(moved)) rescale_o<D, NT>(st, alpha);
+      pv_tile<D, NT, NKT>(st, v_prev, rd, p_a);
     }
-
-    if (wave_active && k0 <= wave_last_key) {
-      f32x16 s[BC / 32][NT];
-      scores_tile<D, NT, BC / 32>(s, k_cur, 0, st.qf, m32, hh);
-
-      const bool edge = (k0 + BC > Lk) || (CAUSAL && k0 + BC - 1 > qw0 + delta);
-      if (edge) {
+    if (j < wn) {
+      f32x16 s[NKT][NT];
+      scores_tile<D, NT, NKT, false>(s, k_cur, rd, st.qf);
+      if (edge_tile(j)) {
+        // key k0 + kt*32 + 4 hh + c_v (c_v = (v & 3) + 8 (v >> 2)) is admissible
+        // for query qi when it is <= min(Lk - 1, qi + Lk - Lq) (causal) or
+        // <= Lk - 1: one compare per element against a per-lane limit
+        const int kbase = j * BC + 4 * hh;
 #pragma unroll
-        for (int kt = 0; kt < BC / 32; ++kt)
+        for (int t = 0; t < NT; ++t) {
+          const int qi = qw0 + t * 32 + m32;
+          const int lim = (CAUSAL ? min(Lk - 1, qi + delta) : Lk - 1) - kbase;
 #pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const int qi = qw0 + t * 32 + m32;
+          for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int key = k0 + kt * 32 + acc_row(v, hh);
-              const bool ok = key < Lk && (!CAUSAL || key <= qi + delta);
-              if (!ok) s[kt][t][v] = -INFINITY;
-            }
-          }
+            for (int v = 0; v < 16; ++v)
+              if ((v & 3) + 8 * (v >> 2) + 32 * kt > lim) s[kt][t][v] = -INFINITY;
+        }
       }
+      moved = softmax_probs<D, NT, NKT>(st, s, p_a, alpha, p.c);
+    }
+  };
 
-      bf16x8 pb[BC / 32][NT][2];
-      softmax_update<D, NT, BC / 32>(st, s, pb, p.c);
-      pv_tile<D, NT, BC / 32>(st, v_cur, 0, pb, lane);
+  int j = 0;
+  // Steady steps: 1 <= j < wn, tile j needs no mask.  Unrolled by two so that
+  // the LDS stages and the probability registers swap statically.
+  // First tile that needs a mask: tile j crosses the end of the keys when
+  // j >= Lk / BC, and (causal) this wave's diagonal when
+  // j >= (qw0 + Lk - Lq + 1) / BC.
+  int steady_end = min(wn, Lk / BC);
+  if (CAUSAL) steady_end = min(steady_end, (qw0 + delta + 1) / BC);
+  auto steady_ok = [&](int jj) { return jj < steady_end; };
+  if (steady_ok(0) && wn > 1) {
+    general_step(0);  // softmax of S_0 -> p_a
+    j = 1;
+#pragma clang loop unroll(disable)
+    while (steady_ok(j)) {
+      // odd j: K_j in stage 1, V_{j-1} in stage 0, P_{j-1} in p_a
+      stage(j);
+      if (__any(moved)) rescale_o<D, NT>(st, alpha);
+      moved = steady_step<D, NT>(st, k_lds1, v_lds0, rd, p_a, p_b, alpha, p.c);
+      ++j;
+      if (!steady_ok(j)) {
+        // the generic step expects P_{j-1} in p_a
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) p_a[kt][t][u] = p_b[kt][t][u];
+        break;
+      }
+      // even j: K_j in stage 0, V_{j-1} in stage 1, P_{j-1} in p_b
+      stage(j);
+      if (__any(moved)) rescale_o<D, NT>(st, alpha);
+      moved = steady_step<D, NT>(st, k_lds0, v_lds1, rd, p_b, p_a, alpha, p.c);
+      ++j;
     }
   }
+#pragma clang loop unroll(disable)
+  for (; j <= n_kt; ++j) general_step(j);
 
-  // ---- epilogue: O / l, LSE = ln 2 * (m c + log2 l) ----
+  // ---- epilogue: O / l, LSE = ln 2 * (r c + log2 l) ----
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const float lt = halfwave_sum(st.l[t]);
