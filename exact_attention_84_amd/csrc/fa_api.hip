@@ -8,7 +8,7 @@
 
 #include <atomic>
 
-#include "../../include/fa.h"
+#include "fa.h"
 #include "fa_internal.hpp"
 
 namespace {
@@ -142,7 +142,10 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   if (varlen && !cu_seqlens_q) return fail(FA_ERR_NULL, "cu_seqlens_q is NULL");
   const int br = fa::fwd_block_rows(head_dim);
   const long long n_qtiles = (rows_q + br - 1) / br;
-  const long long total = (long long)batch * heads_q * n_qtiles;
+  // causal query tiles of fixed-length batches are processed in pairs
+  // (heavy with light)
+  const long long n_items = (causal && !varlen) ? (n_qtiles + 1) / 2 : n_qtiles;
+  const long long total = (long long)batch * heads_q * n_items;
   if (total > 0x7fffffffLL) return fail(FA_ERR_SHAPE, "too many query tiles");
   if (total == 0) return ok();  // nothing to compute
 
@@ -163,6 +166,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   p.seqlen_q = seqlen_q;
   p.seqlen_k = seqlen_k;
   p.n_qtiles = (int)n_qtiles;
+  p.n_items = (int)n_items;
   p.total = (int)total;
   p.c = scale * fa::kLog2eHost;
   p.o_f32 = o_dtype == FA_DTYPE_F32;

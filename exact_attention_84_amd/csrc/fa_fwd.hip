@@ -122,7 +122,7 @@ __device__ __forceinline__ bool steady_step(WaveState<D, NT>& st, const char* __
 
 // Two waves per SIMD (256 registers each) when a wave owns 32 query rows, so
 // that one wave's MFMAs overlap the other's softmax arithmetic.
-template <int D, int NW, int NT, bool CAUSAL>
+template <int D, int NW, int NT, bool CAUSAL, bool PAIR>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
 void fwd_kernel(const FwdParams p) {
   constexpr int BC = 64;
@@ -145,15 +145,13 @@ void fwd_kernel(const FwdParams p) {
 
   // ---- work item: (sequence b, kv head, query head in group, query tile) ----
   const int item = xcd_remap(blockIdx.x, p.total);
-  const int qt_r = item % p.n_qtiles;
-  int rest = item / p.n_qtiles;
+  const int it = item % p.n_items;
+  int rest = item / p.n_items;
   const int hg = rest % p.group;
   rest /= p.group;
   const int kvh = rest % p.hkv;
   const int b = rest / p.hkv;
   const int h = kvh * p.group + hg;
-  // Causal tiles are heaviest at the end of the sequence: start those first.
-  const int qt = CAUSAL ? p.n_qtiles - 1 - qt_r : qt_r;
 
   int q_start, Lq, k_start, Lk;
   if (p.cu_q) {
@@ -167,8 +165,9 @@ void fwd_kernel(const FwdParams p) {
     k_start = b * p.seqlen_k;
     Lk = p.seqlen_k;
   }
+  // One query tile, as a function of its index, inlined at its one call site.
+  auto run_tile = [&](const int qt) __attribute__((always_inline)) {
   const int q0 = qt * BR;
-  if (q0 >= Lq) return;  // packed sequence shorter than this tile (uniform)
 
   const int delta = Lk - Lq;  // bottom-right causal offset
   int n_kt = (Lk + BC - 1) / BC;
@@ -335,19 +334,38 @@ void fwd_kernel(const FwdParams p) {
       if (hh == 0) p.lse[orow] = lse;
     }
   }
+  };  // run_tile
+
+  if constexpr (PAIR) {
+    // Causal, fixed length: under the diagonal tile i costs about i + 1 key
+    // tiles, so tile n-1-i (heaviest first) is paired with tile i and every
+    // workgroup gets the same amount of work.
+    const int first = p.n_qtiles - 1 - it;
+    run_tile(first);
+    if (it < first) {
+      __syncthreads();  // every wave is done with the first tile's LDS stages
+      run_tile(it);
+    }
+  } else {
+    // One tile; causal tiles heaviest first.
+    const int qt = CAUSAL ? p.n_qtiles - 1 - it : it;
+    if (qt * BR < Lq) run_tile(qt);  // a packed sequence may be shorter (uniform)
+  }
 }
 
 // Explicit instantiations: every kernel the dispatcher can launch is emitted
 // on both the device and the host side.
-template __global__ void fwd_kernel<128, kFwdWaves, kFwdNT, false>(const FwdParams);
-template __global__ void fwd_kernel<128, kFwdWaves, kFwdNT, true>(const FwdParams);
-template __global__ void fwd_kernel<64, kFwdWaves, kFwdNT, false>(const FwdParams);
-template __global__ void fwd_kernel<64, kFwdWaves, kFwdNT, true>(const FwdParams);
+template __global__ void fwd_kernel<128, kFwdWaves, kFwdNT, false, false>(const FwdParams);
+template __global__ void fwd_kernel<128, kFwdWaves, kFwdNT, true, false>(const FwdParams);
+template __global__ void fwd_kernel<128, kFwdWaves, kFwdNT, true, true>(const FwdParams);
+template __global__ void fwd_kernel<64, kFwdWaves, kFwdNT, false, false>(const FwdParams);
+template __global__ void fwd_kernel<64, kFwdWaves, kFwdNT, true, false>(const FwdParams);
+template __global__ void fwd_kernel<64, kFwdWaves, kFwdNT, true, true>(const FwdParams);
 
-template <int D, int NW, int NT, bool CAUSAL>
+template <int D, int NW, int NT, bool CAUSAL, bool PAIR>
 static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_kernel<D, NW, NT, CAUSAL>), dim3(p.total), dim3(NW * 64), 0, stream,
-                     p);
+  hipLaunchKernelGGL((fwd_kernel<D, NW, NT, CAUSAL, PAIR>), dim3(p.total), dim3(NW * 64), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -356,12 +374,15 @@ int fwd_block_rows(int head_dim) {
   return kFwdWaves * 32 * kFwdNT;
 }
 
+template <int D>
+static hipError_t launch_d(const FwdParams& p, bool causal, hipStream_t stream) {
+  if (!causal) return launch_one<D, kFwdWaves, kFwdNT, false, false>(p, stream);
+  if (p.cu_q) return launch_one<D, kFwdWaves, kFwdNT, true, false>(p, stream);
+  return launch_one<D, kFwdWaves, kFwdNT, true, true>(p, stream);
+}
+
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, hipStream_t stream) {
-  if (head_dim == 128)
-    return causal ? launch_one<128, kFwdWaves, kFwdNT, true>(p, stream)
-                  : launch_one<128, kFwdWaves, kFwdNT, false>(p, stream);
-  return causal ? launch_one<64, kFwdWaves, kFwdNT, true>(p, stream)
-                : launch_one<64, kFwdWaves, kFwdNT, false>(p, stream);
+  return head_dim == 128 ? launch_d<128>(p, causal, stream) : launch_d<64>(p, causal, stream);
 }
 
 }  // namespace fa

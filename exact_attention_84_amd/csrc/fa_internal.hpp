@@ -35,7 +35,9 @@ struct FwdParams {
   const int32_t* cu_k;
   int hq, hkv, group;
   int seqlen_q, seqlen_k;  // fixed-length mode
-  int n_qtiles;            // query tiles per (sequence, head)
+  int n_qtiles;            // query tiles per (sequence, head), longest sequence
+  int n_items;             // workgroups per (sequence, head): n_qtiles, or
+                           // ceil(n_qtiles / 2) when causal tiles are paired
   int total;               // workgroups
   float c;                 // scale * log2(e)
   int o_f32;
