@@ -64,6 +64,48 @@ def measured_traffic(kernel: str):
     return None if k is None else k.get("bytes_per_launch")
 
 
+def write_traffic(fetch_dir: str, write_dir: str) -> dict:
+    """Turn two rocprofv3 counter runs of ``bench.py --probe`` (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch) into HBM bytes per launch of the forward
+    kernels.  Each counter is scaled by what it reads for the probe's plain
+    1 GiB copy, which reads and writes exactly 1 GiB."""
+    import csv
+    import statistics
+
+    def per_kernel(d, counter):
+        vals = {}
+        with open(os.path.join(d, "run_counter_collection.csv")) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: statistics.mean(v) for k, v in vals.items()}
+
+    copy_bytes = float(1 << 30)
+    out = {"source_hash": kernel_source_hash(), "kernels": {}, "scale": {}}
+    per = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        kib = per_kernel(d, counter)
+        copy = [v for k, v in kib.items() if "copyBuffer" in k]
+        if not copy:
+            raise SystemExit(f"no copy kernel in {d}: run bench.py --probe under rocprofv3")
+        factor = copy_bytes / (copy[0] * 1024.0)
+        out["scale"][counter] = round(factor, 4)
+        for k, v in kib.items():
+            per.setdefault(k, {})[counter] = v * 1024.0 * factor
+    names = {"fwd_kernel<128, 4, 1, false, false>": "fwd_noncausal_d128",
+             "fwd_kernel<128, 4, 1, true, true>": "fwd_causal_d128"}
+    for k, v in per.items():
+        for pat, tag in names.items():
+            if pat in k and "FETCH_SIZE" in v and "WRITE_SIZE" in v:
+                out["kernels"][tag] = {"kernel": k, "read_bytes": round(v["FETCH_SIZE"]),
+                                       "write_bytes": round(v["WRITE_SIZE"]),
+                                       "bytes_per_launch": round(v["FETCH_SIZE"] +
+                                                                 v["WRITE_SIZE"])}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    return out
+
+
 def to_dev(bits):
     import torch
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
@@ -206,15 +248,21 @@ def cpu_baseline(w, budget_s=15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--probe", action="store_true",
                     help="counter-collection mode: only the timed launches of the headline "
                          "workload plus a plain 1 GiB device copy (the scale for HBM byte "
                          "counters); prints no JSON")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc runs of --probe "
+                         "(FETCH_SIZE, then WRITE_SIZE) and exit; needs no GPU")
     a = ap.parse_args()
+    if a.write_traffic:
+        print(json.dumps(write_traffic(*a.write_traffic), indent=1))
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
               "(the attention forward here runs whole on a single MI355X)", file=sys.stderr)
@@ -303,7 +351,7 @@ def main():
     }
     del o_nc, o_c, lse_nc, lse_c
     if not a.no_extra:
-        res["other_workloads"] = other_workloads(fa, max(5, a.steps // 5), 3)
+        res["other_workloads"] = other_workloads(fa, max(5, a.steps // 5), max(3, a.warmup // 5))
     if not a.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w)
         log("cpu_baseline", res["cpu_baseline"])
