@@ -142,9 +142,8 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   if (varlen && !cu_seqlens_q) return fail(FA_ERR_NULL, "cu_seqlens_q is NULL");
   const int br = fa::fwd_block_rows(head_dim);
   const long long n_qtiles = (rows_q + br - 1) / br;
-  // causal query tiles of fixed-length batches are processed in pairs
-  // (heavy with light)
-  const long long n_items = (causal && !varlen) ? (n_qtiles + 1) / 2 : n_qtiles;
+  // causal query tiles are processed in pairs (heavy with light), per sequence
+  const long long n_items = causal ? (n_qtiles + 1) / 2 : n_qtiles;
   const long long total = (long long)batch * heads_q * n_items;
   if (total > 0x7fffffffLL) return fail(FA_ERR_SHAPE, "too many query tiles");
   if (total == 0) return ok();  // nothing to compute

@@ -85,14 +85,20 @@ __device__ __forceinline__ int swap_bits23(int k) {
 // store) both fall on distinct bank groups.
 __device__ __forceinline__ int vt_swizzle(int d) { return (d & 7) ^ ((d >> 3) & 7); }
 
-// Workgroup id -> work-item id so that consecutive work items run on the same
-// XCD (MI355X hands workgroups to its 8 XCDs round-robin).  Consecutive items
-// share K/V, which then stays in that XCD's L2.
-__device__ __forceinline__ int xcd_remap(int w, int total) {
-  const int per = total >> 3, rem = total & 7;
+// Workgroup id -> work-item id.  MI355X hands workgroups to its 8 XCDs
+// round-robin (workgroup w runs on XCD w mod 8), and each XCD has its own L2.
+// Work items come in groups of `gs` consecutive items that read the same K/V
+// (one sequence and kv head).  Groups are dealt to the XCDs round-robin, so
+// a group's items stay on one XCD and share K/V in its L2, while groups of
+// different cost (packed sequences of different lengths) spread over all
+// XCDs.  Groups left over after the last full round of 8 keep the identity
+// order.  The map is a bijection on [0, total) when total is a multiple of gs.
+__device__ __forceinline__ int xcd_remap(int w, int total, int gs) {
+  const int full = (total / gs) >> 3;  // complete rounds of 8 groups
+  if (w >= full * 8 * gs) return w;
   const int x = w & 7, slot = w >> 3;
-  const int base = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
-  return base + slot;
+  const int r = slot / gs, within = slot - r * gs;
+  return (r * 8 + x) * gs + within;
 }
 
 // ---------------------------------------------------------------------------

@@ -144,7 +144,7 @@ void fwd_kernel(const FwdParams p) {
   const int m32 = lane & 31, hh = lane >> 5;
 
   // ---- work item: (sequence b, kv head, query head in group, query tile) ----
-  const int item = xcd_remap(blockIdx.x, p.total);
+  const int item = xcd_remap(blockIdx.x, p.total, p.group * p.n_items);
   const int it = item % p.n_items;
   int rest = item / p.n_items;
   const int hg = rest % p.group;
@@ -337,29 +337,27 @@ void fwd_kernel(const FwdParams p) {
   };  // run_tile
 
   if constexpr (PAIR) {
-    // Causal, fixed length: under the diagonal tile i costs about i + 1 key
-    // tiles, so tile n-1-i (heaviest first) is paired with tile i and every
-    // workgroup gets the same amount of work.
-    const int first = p.n_qtiles - 1 - it;
+    // Causal: under the diagonal tile i of a sequence with n tiles costs about
+    // i + 1 key tiles, so tile n-1-i (heaviest first) is paired with tile i
+    // and every workgroup of the sequence gets n + 1 key tiles of work.  n is
+    // this sequence's own tile count, so packed sequences pair the same way.
+    const int first = (Lq + BR - 1) / BR - 1 - it;
+    if (first < it) return;  // past the middle of a shorter sequence (uniform)
     run_tile(first);
     if (it < first) {
       __syncthreads();  // every wave is done with the first tile's LDS stages
       run_tile(it);
     }
   } else {
-    // One tile; causal tiles heaviest first.
-    const int qt = CAUSAL ? p.n_qtiles - 1 - it : it;
-    if (qt * BR < Lq) run_tile(qt);  // a packed sequence may be shorter (uniform)
+    if (it * BR < Lq) run_tile(it);
   }
 }
 
 // Explicit instantiations: every kernel the dispatcher can launch is emitted
 // on both the device and the host side.
 template __global__ void fwd_kernel<128, kFwdWaves, kFwdNT, false, false>(const FwdParams);
-template __global__ void fwd_kernel<128, kFwdWaves, kFwdNT, true, false>(const FwdParams);
 template __global__ void fwd_kernel<128, kFwdWaves, kFwdNT, true, true>(const FwdParams);
 template __global__ void fwd_kernel<64, kFwdWaves, kFwdNT, false, false>(const FwdParams);
-template __global__ void fwd_kernel<64, kFwdWaves, kFwdNT, true, false>(const FwdParams);
 template __global__ void fwd_kernel<64, kFwdWaves, kFwdNT, true, true>(const FwdParams);
 
 template <int D, int NW, int NT, bool CAUSAL, bool PAIR>
@@ -376,9 +374,8 @@ int fwd_block_rows(int head_dim) {
 
 template <int D>
 static hipError_t launch_d(const FwdParams& p, bool causal, hipStream_t stream) {
-  if (!causal) return launch_one<D, kFwdWaves, kFwdNT, false, false>(p, stream);
-  if (p.cu_q) return launch_one<D, kFwdWaves, kFwdNT, true, false>(p, stream);
-  return launch_one<D, kFwdWaves, kFwdNT, true, true>(p, stream);
+  return causal ? launch_one<D, kFwdWaves, kFwdNT, true, true>(p, stream)
+                : launch_one<D, kFwdWaves, kFwdNT, false, false>(p, stream);
 }
 
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, hipStream_t stream) {
