@@ -48,6 +48,11 @@ FIXED_CASES = [
     (1, 129, 129, 8, 2, 128, False),
     (1, 64, 700, 2, 2, 128, False),
     (2, 200, 0, 2, 2, 64, False),     # no keys at all: O = 0, LSE = -inf
+    # more than 8 (sequence, kv-head) groups, not a multiple of 8: the
+    # workgroup -> XCD remap deals 8-group rounds and keeps the rest in order
+    (3, 200, 200, 6, 3, 128, True),
+    (3, 200, 200, 6, 3, 128, False),
+    (5, 130, 130, 4, 4, 64, True),
 ]
 
 
@@ -70,6 +75,8 @@ VARLEN_CASES = [
     ([1, 17, 300, 0, 129, 64, 65], None, 4, 2, 128),
     ([5, 250, 3, 77], [9, 300, 1, 77], 8, 2, 128),   # separate key lengths
     ([130, 1, 64], None, 2, 1, 64),
+    # 10 sequences x 2 kv heads = 20 groups (two full rounds of 8, 4 left)
+    ([300, 1, 513, 128, 129, 0, 257, 64, 700, 33], None, 4, 2, 128),
 ]
 
 
