@@ -21,6 +21,21 @@
 
 namespace fa {
 
+// Sets to -inf every score of a 64-key tile whose key lies past the lane's
+// limit.  Key kt*32 + 4 hh + c_v (c_v = (v & 3) + 8 (v >> 2)) of the tile is
+// admissible for the query of lane (t, m32) when its offset from the tile's
+// first key, minus 4 hh, is <= lim[t]: one compare per element.
+template <int NT, int NKT>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[NKT][NT], const int (&lim)[NT]) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if ((v & 3) + 8 * (v >> 2) + 32 * kt > lim[t]) s[kt][t][v] = -INFINITY;
+}
+
 // One steady-state step of a wave owning NT groups of 32 query rows, 64-key
 // tiles:
 //   s      = Q K_j^T            (D/8 K fragments, NT MFMAs each)
@@ -30,12 +45,14 @@ namespace fa {
 // by a slice of the softmax of s (sched_barrier fences keep that order): the
 // wave keeps issuing ALU instructions while the matrix core works.  Returns
 // whether a row moved its reference (alpha then holds the rescale factors).
+// A tile that crosses the end of the keys or the diagonal is masked first
+// (`masked`, uniform over the wave; limits as in mask_tile).
 template <int D, int NT>
 __device__ __forceinline__ bool steady_step(WaveState<D, NT>& st, const char* __restrict__ k_cur,
                                             const char* __restrict__ v_prev, const LdsRead<D>& rd,
                                             const bf16x8 (&pin)[2][NT][2],
                                             bf16x8 (&pout)[2][NT][2], float (&alpha)[NT],
-                                            float c) {
+                                            float c, bool masked, const int (&lim)[NT]) {
   constexpr int DT = D / 32;
   constexpr int SLOTS = D / 8;                  // V fragments per step
   constexpr int LEAD = 2;                       // P V MFMAs before the first slice
@@ -46,6 +63,7 @@ __device__ __forceinline__ bool steady_step(WaveState<D, NT>& st, const char* __
 
   f32x16 s[2][NT];
   scores_tile<D, NT, 2>(s, k_cur, rd, st.qf);
+  if (masked) mask_tile<NT, 2>(s, lim);
 
   float mx[NT], msub[NT], rs[NT], mref[NT];
   uint32_t pk[NT][16];
@@ -212,6 +230,15 @@ void fwd_kernel(const FwdParams p) {
     const int k0 = j * BC;
     return (k0 + BC > Lk) || (CAUSAL && k0 + BC - 1 > qw0 + delta);
   };
+  // Last admissible key of each of this lane's query rows, min(Lk - 1,
+  // qi + Lk - Lq) causal or Lk - 1, minus 4 hh (the lane's key offset in a
+  // tile); tile j masks against row_lim - j * BC.
+  int row_lim[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int qi = qw0 + t * 32 + m32;
+    row_lim[t] = (CAUSAL ? min(Lk - 1, qi + delta) : Lk - 1) - 4 * hh;
+  }
   // Step j: K_j and V_{j-1} are in LDS; K_{j+1} and V_j start streaming into
   // the stages that K_{j-1} and V_{j-2} used.
   auto stage = [&](int j) {
@@ -243,45 +270,40 @@ void fwd_kernel(const FwdParams p) {
       f32x16 s[NKT][NT];
       scores_tile<D, NT, NKT, false>(s, k_cur, rd, st.qf);
       if (edge_tile(j)) {
-        // key k0 + kt*32 + 4 hh + c_v (c_v = (v & 3) + 8 (v >> 2)) is admissible
-        // for query qi when it is <= min(Lk - 1, qi + Lk - Lq) (causal) or
-        // <= Lk - 1: one compare per element against a per-lane limit
-        const int kbase = j * BC + 4 * hh;
+        int lim[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const int qi = qw0 + t * 32 + m32;
-          const int lim = (CAUSAL ? min(Lk - 1, qi + delta) : Lk - 1) - kbase;
-#pragma unroll
-          for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-              if ((v & 3) + 8 * (v >> 2) + 32 * kt > lim) s[kt][t][v] = -INFINITY;
-        }
+        for (int t = 0; t < NT; ++t) lim[t] = row_lim[t] - j * BC;
+        mask_tile<NT, NKT>(s, lim);
       }
       moved = softmax_probs<D, NT, NKT>(st, s, p_a, alpha, p.c);
     }
   };
 
   int j = 0;
-  // Steady steps: 1 <= j < wn, tile j needs no mask.  Unrolled by two so that
-  // the LDS stages and the probability registers swap statically.
-  // First tile that needs a mask: tile j crosses the end of the keys when
-  // j >= Lk / BC, and (causal) this wave's diagonal when
-  // j >= (qw0 + Lk - Lq + 1) / BC.
-  int steady_end = min(wn, Lk / BC);
-  if (CAUSAL) steady_end = min(steady_end, (qw0 + delta + 1) / BC);
-  auto steady_ok = [&](int jj) { return jj < steady_end; };
-  if (steady_ok(0) && wn > 1) {
+  // Steady steps: 1 <= j < wn, each one the scores of tile j and the P V of
+  // tile j-1, masked when tile j crosses the end of the keys or this wave's
+  // diagonal.  Unrolled by two so that the LDS stages and the probability
+  // registers swap statically.  Step 0 (no P V yet), the final P V and the
+  // steps where this wave has no tile left (the workgroup's other waves
+  // still do) take the generic path.
+  auto steady = [&](int jj, const char* k_cur, const char* v_prev, const bf16x8 (&pin)[NKT][NT][2],
+                    bf16x8 (&pout)[NKT][NT][2]) {
+    stage(jj);
+    if (__any(moved)) rescale_o<D, NT>(st, alpha);
+    int lim[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) lim[t] = row_lim[t] - jj * BC;
+    moved = steady_step<D, NT>(st, k_cur, v_prev, rd, pin, pout, alpha, p.c, edge_tile(jj), lim);
+  };
+  if (wn > 1) {
     general_step(0);  // softmax of S_0 -> p_a
     j = 1;
 #pragma clang loop unroll(disable)
-    while (steady_ok(j)) {
+    while (j < wn) {
       // odd j: K_j in stage 1, V_{j-1} in stage 0, P_{j-1} in p_a
-      stage(j);
-      if (__any(moved)) rescale_o<D, NT>(st, alpha);
-      moved = steady_step<D, NT>(st, k_lds1, v_lds0, rd, p_a, p_b, alpha, p.c);
+      steady(j, k_lds1, v_lds0, p_a, p_b);
       ++j;
-      if (!steady_ok(j)) {
+      if (j >= wn) {
         // the generic step expects P_{j-1} in p_a
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
@@ -292,9 +314,7 @@ void fwd_kernel(const FwdParams p) {
         break;
       }
       // even j: K_j in stage 0, V_{j-1} in stage 1, P_{j-1} in p_b
-      stage(j);
-      if (__any(moved)) rescale_o<D, NT>(st, alpha);
-      moved = steady_step<D, NT>(st, k_lds0, v_lds1, rd, p_b, p_a, alpha, p.c);
+      steady(j, k_lds0, v_lds1, p_b, p_a);
       ++j;
     }
   }
