@@ -92,8 +92,8 @@ def write_traffic(fetch_dir: str, write_dir: str) -> dict:
         out["scale"][counter] = round(factor, 4)
         for k, v in kib.items():
             per.setdefault(k, {})[counter] = v * 1024.0 * factor
-    names = {"fwd_kernel<128, 4, 1, false, false>": "fwd_noncausal_d128",
-             "fwd_kernel<128, 4, 1, true, true>": "fwd_causal_d128"}
+    names = {"fwd_kernel<128, 8, 1, false, false>": "fwd_noncausal_d128",
+             "fwd_kernel<128, 8, 1, true, true>": "fwd_causal_d128"}
     for k, v in per.items():
         for pat, tag in names.items():
             if pat in k and "FETCH_SIZE" in v and "WRITE_SIZE" in v:
@@ -321,7 +321,7 @@ def main():
     log(f"step {ms_step:.4f} ms ({wall / a.steps * 1e3:.4f} ms wall), non-causal {ms_nc:.4f} ms "
         f"({ach:.1f} TFLOP/s), causal {ms_c:.4f} ms ({fl_c / (ms_c * 1e-3) / 1e12:.1f} TFLOP/s)")
 
-    kname = "fwd_kernel<128, 4, 1, false, false>"
+    kname = "fwd_kernel<128, 8, 1, false, false>"
     traffic = measured_traffic("fwd_noncausal_d128")
     res = {
         "metric": METRIC,

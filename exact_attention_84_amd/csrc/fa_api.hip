@@ -140,7 +140,8 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   if ((!k || !v) && (long long)batch * rows_k > 0)
     return fail(FA_ERR_NULL, "k and v must be non-NULL");
   if (varlen && !cu_seqlens_q) return fail(FA_ERR_NULL, "cu_seqlens_q is NULL");
-  const int br = fa::fwd_block_rows(head_dim);
+  const int waves = fa::fwd_waves(head_dim, varlen, rows_q);
+  const int br = fa::fwd_block_rows(waves);
   const long long n_qtiles = (rows_q + br - 1) / br;
   // causal query tiles are processed in pairs (heavy with light), per sequence
   const long long n_items = causal ? (n_qtiles + 1) / 2 : n_qtiles;
@@ -167,6 +168,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   p.n_qtiles = (int)n_qtiles;
   p.n_items = (int)n_items;
   p.total = (int)total;
+  p.waves = waves;
   p.c = scale * fa::kLog2eHost;
   p.o_f32 = o_dtype == FA_DTYPE_F32;
   hipError_t e = fa::launch_fwd(p, head_dim, causal != 0, static_cast<hipStream_t>(stream));

@@ -375,10 +375,12 @@ void fwd_kernel(const FwdParams p) {
 
 // Explicit instantiations: every kernel the dispatcher can launch is emitted
 // on both the device and the host side.
-template __global__ void fwd_kernel<128, kFwdWaves, kFwdNT, false, false>(const FwdParams);
-template __global__ void fwd_kernel<128, kFwdWaves, kFwdNT, true, true>(const FwdParams);
-template __global__ void fwd_kernel<64, kFwdWaves, kFwdNT, false, false>(const FwdParams);
-template __global__ void fwd_kernel<64, kFwdWaves, kFwdNT, true, true>(const FwdParams);
+template __global__ void fwd_kernel<128, 4, kFwdNT, false, false>(const FwdParams);
+template __global__ void fwd_kernel<128, 4, kFwdNT, true, true>(const FwdParams);
+template __global__ void fwd_kernel<128, 8, kFwdNT, false, false>(const FwdParams);
+template __global__ void fwd_kernel<128, 8, kFwdNT, true, true>(const FwdParams);
+template __global__ void fwd_kernel<64, 4, kFwdNT, false, false>(const FwdParams);
+template __global__ void fwd_kernel<64, 4, kFwdNT, true, true>(const FwdParams);
 
 template <int D, int NW, int NT, bool CAUSAL, bool PAIR>
 static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
@@ -387,19 +389,22 @@ static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-int fwd_block_rows(int head_dim) {
-  (void)head_dim;
-  return kFwdWaves * 32 * kFwdNT;
+int fwd_waves(int head_dim, bool varlen, int seqlen_q) {
+  return (head_dim == 128 && !varlen && seqlen_q >= 2048) ? 8 : 4;
 }
 
-template <int D>
-static hipError_t launch_d(const FwdParams& p, bool causal, hipStream_t stream) {
-  return causal ? launch_one<D, kFwdWaves, kFwdNT, true, true>(p, stream)
-                : launch_one<D, kFwdWaves, kFwdNT, false, false>(p, stream);
+int fwd_block_rows(int waves) { return waves * 32 * kFwdNT; }
+
+template <int D, int NW>
+static hipError_t launch_dw(const FwdParams& p, bool causal, hipStream_t stream) {
+  return causal ? launch_one<D, NW, kFwdNT, true, true>(p, stream)
+                : launch_one<D, NW, kFwdNT, false, false>(p, stream);
 }
 
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, hipStream_t stream) {
-  return head_dim == 128 ? launch_d<128>(p, causal, stream) : launch_d<64>(p, causal, stream);
+  if (head_dim == 64) return launch_dw<64, 4>(p, causal, stream);
+  return p.waves == 8 ? launch_dw<128, 8>(p, causal, stream)
+                      : launch_dw<128, 4>(p, causal, stream);
 }
 
 }  // namespace fa

@@ -7,15 +7,11 @@
 
 namespace fa {
 
-// Prefill tile shape: kFwdWaves waves per workgroup, each owning kFwdNT
-// groups of 32 query rows; K/V tiles of 64 keys.
-#ifndef FA_FWD_WAVES
-#define FA_FWD_WAVES 4
-#endif
+// Prefill tile shape: 4 or 8 waves per workgroup (fwd_waves), each owning
+// kFwdNT groups of 32 query rows; K/V tiles of 64 keys.
 #ifndef FA_FWD_NT
 #define FA_FWD_NT 1
 #endif
-constexpr int kFwdWaves = FA_FWD_WAVES;
 constexpr int kFwdNT = FA_FWD_NT;
 
 // Split-KV decode: a workgroup of 4 waves takes 128 keys per step, 32 per wave.
@@ -39,6 +35,7 @@ struct FwdParams {
   int n_items;             // workgroups per (sequence, head): n_qtiles, or
                            // ceil(n_qtiles / 2) when causal tiles are paired
   int total;               // workgroups
+  int waves;               // waves per workgroup (4 or 8)
   float c;                 // scale * log2(e)
   int o_f32;
 };
@@ -58,7 +55,12 @@ struct DecodeParams {
   float c;
 };
 
-int fwd_block_rows(int head_dim);
+// Waves per prefill workgroup: 8 (256 query rows, half the K/V loads per
+// query) for fixed-length batches of at least 2048 queries at head_dim 128,
+// else 4 (128 rows; less padding and more workgroups for short or packed
+// sequences).
+int fwd_waves(int head_dim, bool varlen, int seqlen_q);
+int fwd_block_rows(int waves);
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_combine(const float* o_part, const float* lse_part, int rows, int n_splits,
