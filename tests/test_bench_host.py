@@ -1,0 +1,83 @@
+"""Host-side parts of bench.py (no GPU): the --gpus guard, the conversion of
+rocprofv3 counter files into bytes per launch, the source-hash check that
+voids stale traffic figures, and the CPU oracle baseline's sample."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FIELDS = ["Correlation_Id", "Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def write_counters(d, counter, rows):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (name, val) in enumerate(rows):
+            w.writerow({"Correlation_Id": i, "Dispatch_Id": i, "Kernel_Name": name,
+                        "Counter_Name": counter, "Counter_Value": val})
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_write_traffic_scales_by_the_copy_kernel(tmp_path, monkeypatch):
+    nc = "void fa::fwd_kernel<128, 8, 1, false, false>(fa::FwdParams)"
+    ca = "void fa::fwd_kernel<128, 8, 1, true, true>(fa::FwdParams)"
+    cp = "__amd_rocclr_copyBuffer"
+    # the copy moves 2^30 bytes each way; FETCH_SIZE reads half of it (x2),
+    # WRITE_SIZE all of it (x1), in KiB
+    write_counters(tmp_path / "f", "FETCH_SIZE",
+                   [(nc, 1000.0), (nc, 1002.0), (ca, 500.0), (cp, 524288.0)])
+    write_counters(tmp_path / "w", "WRITE_SIZE", [(nc, 300.0), (ca, 301.0), (cp, 1048576.0)])
+    out_file = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out_file))
+    t = bench.write_traffic(str(tmp_path / "f"), str(tmp_path / "w"))
+    assert t["scale"] == {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
+    k = t["kernels"]["fwd_noncausal_d128"]
+    assert k["read_bytes"] == round(1001.0 * 1024 * 2)
+    assert k["write_bytes"] == 300 * 1024
+    assert k["bytes_per_launch"] == k["read_bytes"] + k["write_bytes"]
+    assert t["kernels"]["fwd_causal_d128"]["read_bytes"] == 500 * 1024 * 2
+    assert json.loads(out_file.read_text()) == t
+    # read back only while the kernel sources are unchanged
+    assert bench.measured_traffic("fwd_noncausal_d128") == k["bytes_per_launch"]
+    stale = dict(t, source_hash="0" * 16)
+    out_file.write_text(json.dumps(stale))
+    assert bench.measured_traffic("fwd_noncausal_d128") is None
+
+
+def test_write_traffic_needs_the_copy_kernel(tmp_path, monkeypatch):
+    write_counters(tmp_path / "f", "FETCH_SIZE", [("fwd_kernel<128, 8, 1, false, false>", 1.0)])
+    write_counters(tmp_path / "w", "WRITE_SIZE", [("fwd_kernel<128, 8, 1, false, false>", 1.0)])
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "t.json"))
+    with pytest.raises(SystemExit):
+        bench.write_traffic(str(tmp_path / "f"), str(tmp_path / "w"))
+
+
+def test_committed_traffic_file_is_well_formed():
+    with open(bench.TRAFFIC_FILE) as fh:
+        t = json.load(fh)
+    assert len(t["source_hash"]) == 16
+    for k in t["kernels"].values():
+        assert k["bytes_per_launch"] == k["read_bytes"] + k["write_bytes"] > 0
+
+
+def test_cpu_baseline_reports_its_sample():
+    r = bench.cpu_baseline(W.WORKLOADS[1], budget_s=0.05)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
+    assert r["value"] > 0 and r["cores"] >= 1
+    assert "single_head_n256_d64" in r["sample"]
