@@ -78,29 +78,32 @@ def write_traffic(fetch_dir: str, write_dir: str) -> dict:
             for r in csv.DictReader(fh):
                 if r["Counter_Name"] == counter:
                     vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        return {k: statistics.mean(v) for k, v in vals.items()}
+        return vals
 
     copy_bytes = float(1 << 30)
     out = {"source_hash": kernel_source_hash(), "kernels": {}, "scale": {}}
     per = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        kib = per_kernel(d, counter)
-        copy = [v for k, v in kib.items() if "copyBuffer" in k]
+        vals = per_kernel(d, counter)
+        # the 1 GiB copy is the largest copy dispatch (setting up the inputs
+        # launches small ones too)
+        copy = [max(v) for k, v in vals.items() if "copyBuffer" in k]
         if not copy:
             raise SystemExit(f"no copy kernel in {d}: run bench.py --probe under rocprofv3")
-        factor = copy_bytes / (copy[0] * 1024.0)
+        factor = copy_bytes / (max(copy) * 1024.0)
+        kib = {k: statistics.mean(v) for k, v in vals.items()}
         out["scale"][counter] = round(factor, 4)
         for k, v in kib.items():
             per.setdefault(k, {})[counter] = v * 1024.0 * factor
     names = {"fwd_kernel<128, 8, 1, false, false>": "fwd_noncausal_d128",
-             "fwd_kernel<128, 8, 1, true, true>": "fwd_causal_d128"}
+             "fwd_kernel<128, 8, 1, true, true>": "fwd_causal_d128",
+             "decode_kernel<128>": "decode_d128"}
     for k, v in per.items():
         for pat, tag in names.items():
             if pat in k and "FETCH_SIZE" in v and "WRITE_SIZE" in v:
-                out["kernels"][tag] = {"kernel": k, "read_bytes": round(v["FETCH_SIZE"]),
-                                       "write_bytes": round(v["WRITE_SIZE"]),
-                                       "bytes_per_launch": round(v["FETCH_SIZE"] +
-                                                                 v["WRITE_SIZE"])}
+                rd, wr = round(v["FETCH_SIZE"]), round(v["WRITE_SIZE"])
+                out["kernels"][tag] = {"kernel": k, "read_bytes": rd, "write_bytes": wr,
+                                       "bytes_per_launch": rd + wr}
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
     return out
@@ -126,9 +129,12 @@ class LaunchTimer:
         b.record()
         self.pairs.setdefault(name, []).append((a, b))
 
+    def times_ms(self, name):
+        return [a.elapsed_time(b) for a, b in self.pairs.get(name, [])]
+
     def avg_ms(self, name):
-        ps = self.pairs.get(name, [])
-        return sum(a.elapsed_time(b) for a, b in ps) / max(1, len(ps))
+        t = self.times_ms(name)
+        return sum(t) / max(1, len(t))
 
 
 def time_calls(fn, steps, warmup):
@@ -168,6 +174,37 @@ def other_workloads(fa, steps, warmup):
         log(w.name, res[w.name])
         del q, k, v, o, lse
     w = W.WORKLOADS[5]
+    lens, args, kw = decode_inputs(fa, w)
+    ms = time_calls(lambda: fa.decode(*args, scale=w.scale, **kw), steps, warmup)
+    by = W.decode_bytes(w, lens)
+    gbs = by / (ms * 1e-3) / 1e9
+    res[w.name] = {"ms": round(ms, 4), "gbs": round(gbs, 1),
+                   "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4), "gbytes": round(by / 1e9, 3)}
+    log(w.name, res[w.name])
+    return res
+
+
+def cold_launches(fn, n, flush):
+    """Average event-timed duration of `fn` when each launch follows a write
+    of `flush` (512 MiB, twice the 256 MB last-level cache), so that its
+    inputs start in HBM rather than in the MALL."""
+    import torch
+    ts = []
+    for _ in range(n):
+        flush.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        ts.append((a, b))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ts) / n
+
+
+def decode_inputs(fa, w):
+    """Device inputs of the split-KV decode workload (seed 0): query, caches
+    filled up to each drawn length, lengths, outputs and workspace."""
+    import torch
     lens = W.workload_lengths(w, seed=0)
     qd = to_dev(W.decode_q(w.batch, w.heads_q, w.head_dim, seed=0, wid=w.wid))
     kc = torch.zeros((w.batch, w.seqlen_k, w.heads_kv, w.head_dim), dtype=torch.bfloat16,
@@ -177,25 +214,18 @@ def other_workloads(fa, steps, warmup):
         kb, vb = W.decode_kv_slice(b, int(lens[b]), w.heads_kv, w.head_dim, seed=0, wid=w.wid)
         kc[b, :int(lens[b])] = to_dev(kb)
         vc[b, :int(lens[b])] = to_dev(vb)
-    lensd = torch.from_numpy(lens).cuda()
     o = torch.empty_like(qd)
     lse = torch.empty((w.batch, w.heads_q), dtype=torch.float32, device="cuda")
     ws = torch.empty(fa.decode_workspace_size(w.batch, w.heads_q, w.seqlen_k, w.head_dim),
                      dtype=torch.uint8, device="cuda")
-    ms = time_calls(lambda: fa.decode(qd, kc, vc, lensd, scale=w.scale, out=o, lse=lse,
-                                      workspace=ws), steps, warmup)
-    by = W.decode_bytes(w, lens)
-    gbs = by / (ms * 1e-3) / 1e9
-    res[w.name] = {"ms": round(ms, 4), "gbs": round(gbs, 1),
-                   "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4), "gbytes": round(by / 1e9, 3)}
-    log(w.name, res[w.name])
-    return res
+    return lens, (qd, kc, vc, torch.from_numpy(lens).cuda()), dict(out=o, lse=lse, workspace=ws)
 
 
 def probe(fa, w, steps, warmup):
     """Launches for rocprofv3 counter runs: the headline workload's non-causal
-    and causal forward, then a 1 GiB device-to-device copy (a kernel that reads
-    and writes exactly 1 GiB each, to scale the byte counters)."""
+    and causal forward, the split-KV decode workload, then a 1 GiB
+    device-to-device copy (a kernel that reads and writes exactly 1 GiB each,
+    to scale the byte counters)."""
     import torch
     inp = W.make_workload(w, seed=0)
     q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
@@ -204,12 +234,18 @@ def probe(fa, w, steps, warmup):
     for causal in (False, True):
         for _ in range(warmup + steps):
             fa.attention(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse)
+    del q, k, v, o, lse
+    wd = W.WORKLOADS[5]
+    _, args, kw = decode_inputs(fa, wd)
+    for _ in range(warmup + steps):
+        fa.decode(*args, scale=wd.scale, **kw)
+    del args, kw
     a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
     for _ in range(steps):
         b.copy_(a)
     torch.cuda.synchronize()
-    log(f"probe: {warmup + steps} non-causal, {warmup + steps} causal launches, "
+    log(f"probe: {warmup + steps} non-causal, causal and decode launches, "
         f"{steps} copies of {a.numel() * 4} bytes")
 
 
@@ -317,6 +353,11 @@ def main():
     assert torch.isfinite(o_nc.float()).all() and torch.isfinite(o_c.float()).all()
     value = (fl_nc + fl_c) / (ms_step * 1e-3) / 1e12
     ms_nc, ms_c = timer.avg_ms("noncausal"), timer.avg_ms("causal")
+    t_nc = sorted(timer.times_ms("noncausal"))
+    flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
+    ms_cold = cold_launches(lambda: fa.attention(q, k, v, causal=False, scale=w.scale, out=o_nc,
+                                                 lse=lse_nc), 20, flush)
+    del flush
     ach = fl_nc / (ms_nc * 1e-3) / 1e12
     log(f"step {ms_step:.4f} ms ({wall / a.steps * 1e3:.4f} ms wall), non-causal {ms_nc:.4f} ms "
         f"({ach:.1f} TFLOP/s), causal {ms_c:.4f} ms ({fl_c / (ms_c * 1e-3) / 1e12:.1f} TFLOP/s)")
@@ -348,6 +389,10 @@ def main():
                      "flop_per_launch": fl_nc},
         "causal_launch": {"avg_launch_ms": round(ms_c, 5),
                           "tflops": round(fl_c / (ms_c * 1e-3) / 1e12, 2)},
+        "noncausal_launch_ms": {"median": round(t_nc[len(t_nc) // 2], 5),
+                                "min": round(t_nc[0], 5),
+                                "cold_cache_avg": round(ms_cold, 5),
+                                "cold_cache_tflops": round(fl_nc / (ms_cold * 1e-3) / 1e12, 2)},
     }
     del o_nc, o_c, lse_nc, lse_c
     if not a.no_extra:

@@ -40,9 +40,12 @@ def test_write_traffic_scales_by_the_copy_kernel(tmp_path, monkeypatch):
     cp = "__amd_rocclr_copyBuffer"
     # the copy moves 2^30 bytes each way; FETCH_SIZE reads half of it (x2),
     # WRITE_SIZE all of it (x1), in KiB
+    # small copies (input set-up) come with the 1 GiB one; only the largest
+    # sets the scale
     write_counters(tmp_path / "f", "FETCH_SIZE",
-                   [(nc, 1000.0), (nc, 1002.0), (ca, 500.0), (cp, 524288.0)])
-    write_counters(tmp_path / "w", "WRITE_SIZE", [(nc, 300.0), (ca, 301.0), (cp, 1048576.0)])
+                   [(cp, 3.0), (nc, 1000.0), (nc, 1002.0), (ca, 500.0), (cp, 524288.0)])
+    write_counters(tmp_path / "w", "WRITE_SIZE",
+                   [(cp, 6.0), (nc, 300.0), (ca, 301.0), (cp, 1048576.0)])
     out_file = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out_file))
     t = bench.write_traffic(str(tmp_path / "f"), str(tmp_path / "w"))
