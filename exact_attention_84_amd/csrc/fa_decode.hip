@@ -22,14 +22,18 @@ void decode_kernel(const DecodeParams p) {
   constexpr int BC = kDecodeTile;
   constexpr int T = kDecodeWaves * 64;
   static_assert(BC == 32 * kDecodeWaves, "one 32-key sub-tile per wave");
-  using Loader = TileLoader<D, BC, T>;
-  constexpr int KSTR = Loader::KSTR;
-  constexpr int SMEM = Loader::K_ELEMS + Loader::VT_ELEMS;
-  static_assert((kDecodeWaves * kDecodeMaxGroup * (D + 2)) * 4 <= SMEM * 2,
-                "cross-wave merge must fit in the K/V staging area");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
-  uint16_t* k_lds = smem;
-  uint16_t* vt_lds = smem + Loader::K_ELEMS;
+  constexpr int CPR = D / 8;             // 16-byte chunks per key row
+  constexpr int NCH = BC * CPR / T;      // chunks per thread, per tensor
+  constexpr int TILE = BC * D * 2;       // bytes of one K or V tile
+  constexpr int MERGE = kDecodeWaves * kDecodeMaxGroup * (D + 2) * 4;
+  constexpr int SMEM = 2 * TILE > MERGE ? 2 * TILE : MERGE;
+  static_assert(BC * CPR % T == 0, "tile chunks must split evenly over the threads");
+  // K and V tiles row-major with the XOR-swizzled chunk layout of fa_layout.hpp
+  // (conflict-free operand reads on 64 banks); the area is reused for the
+  // cross-wave merge at the end.
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+  char* k_lds = smem;
+  char* v_lds = smem + TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -67,19 +71,48 @@ void decode_kernel(const DecodeParams p) {
       st.qf[0][s] = __builtin_bit_cast(bf16x8, raw);
     }
   }
+  LdsRead<D> rd;
+  rd.init(lane);
 
-  Loader ld;
-  ld.load(kbase, vbase, kv_stride, kbeg, kend, tid);
+  // Next tile staged in registers while this one is used: thread tid moves
+  // chunks tid + i*T (row c / CPR, chunk c % CPR) of K and of V.  Keys past
+  // the end are zero (their scores are masked; zero V rows add nothing).
+  u32x4 kr[NCH], vr[NCH];
+  auto load = [&](int k0) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * T;
+      const int key = k0 + c / CPR;
+      const size_t off = (size_t)key * kv_stride + (c % CPR) * 8;
+      kr[i] = key < kend ? *reinterpret_cast<const u32x4*>(kbase + off) : zero;
+      vr[i] = key < kend ? *reinterpret_cast<const u32x4*>(vbase + off) : zero;
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * T;
+      const int o = kv_offset<D>(c / CPR, c % CPR);
+      *reinterpret_cast<u32x4*>(k_lds + o) = kr[i];
+      *reinterpret_cast<u32x4*>(v_lds + o) = vr[i];
+    }
+  };
+
+  load(kbeg);
   for (int k0 = kbeg; k0 < kend; k0 += BC) {
     __syncthreads();
-    ld.store(k_lds, vt_lds, tid);
+    store();
     __syncthreads();
-    if (k0 + BC < kend) ld.load(kbase, vbase, kv_stride, k0 + BC, kend, tid);
+    if (k0 + BC < kend) load(k0 + BC);
 
     const int ksub = k0 + wave * 32;  // this wave's 32 keys of the tile
     if (ksub < kend) {
       f32x16 s[1][1];
-      scores_subtile<D, 1, KSTR>(s[0], k_lds, wave, st.qf, m32, hh);
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        s[0][0] = mfma_32x32x16(rd.k(k_lds, wave, ks), st.qf[0][ks],
+                                ks == 0 ? f32x16{} : s[0][0]);
       if (ksub + 32 > kend) {
 #pragma unroll
         for (int v = 0; v < 16; ++v)
@@ -87,7 +120,11 @@ void decode_kernel(const DecodeParams p) {
       }
       bf16x8 pb[1][1][2];
       softmax_update<D, 1, 1>(st, s, pb, p.c);
-      pv_subtile<D, 1, BC>(st, vt_lds, wave, pb[0], m32, hh);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          st.o[0][dt] = mfma_32x32x16(rd.v(v_lds, wave, u, dt), pb[0][0][u], st.o[0][dt]);
     }
   }
 

@@ -73,18 +73,6 @@ __device__ __forceinline__ float halfwave_sum(float x) {
 // half-wave hh, for the 32x32 MFMA output layout.
 __device__ __forceinline__ int acc_row(int v, int hh) { return (v & 3) + 8 * (v >> 2) + 4 * hh; }
 
-// Position of key k inside its group of 16 in the V^T tile: bits 2 and 3
-// swapped.  With it, the eight keys a lane contributes to one 16-key step of
-// the P V product are contiguous in LDS.
-__device__ __forceinline__ int swap_bits23(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
-
-// XOR swizzle of the 16-byte chunks of V^T row d.  Eight consecutive rows
-// (one MFMA operand read) and sixteen rows eight apart (one transposing
-// store) both fall on distinct bank groups.
-__device__ __forceinline__ int vt_swizzle(int d) { return (d & 7) ^ ((d >> 3) & 7); }
-
 // Workgroup id -> work-item id.  MI355X hands workgroups to its 8 XCDs
 // round-robin (workgroup w runs on XCD w mod 8), and each XCD has its own L2.
 // Work items come in groups of `gs` consecutive items that read the same K/V
@@ -100,89 +88,6 @@ __device__ __forceinline__ int xcd_remap(int w, int total, int gs) {
   const int r = slot / gs, within = slot - r * gs;
   return (r * 8 + x) * gs + within;
 }
-
-// ---------------------------------------------------------------------------
-// Cooperative K / V tile staging: global -> registers -> LDS.
-//
-// K tile: [BC][D + 8] bf16, row-major, 16 bytes of padding per row so that
-//         the 32 rows of one MFMA operand read fall on distinct banks.
-// V tile: stored transposed, V^T [D][BC], with the key permutation above and
-//         the XOR chunk swizzle, so that an A operand of O^T = V^T P^T is one
-//         16-byte LDS read per lane.
-// Each thread moves whole 16-byte chunks; for V it takes two adjacent keys of
-// the same chunk and interleaves them into 32-bit (key, key+1) pairs.
-// ---------------------------------------------------------------------------
-template <int D, int BC, int T>
-struct TileLoader {
-  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  static constexpr int KSTR = D + 8;                // K row stride, elements
-  static constexpr int NK = (BC * CPR + T - 1) / T;  // K chunks per thread
-  static constexpr int NV = ((BC / 2) * CPR + T - 1) / T;  // V chunk pairs per thread
-  static constexpr int K_ELEMS = BC * KSTR;
-  static constexpr int VT_ELEMS = D * BC;
-  static_assert(BC % 32 == 0 && BC >= 64, "V^T swizzle needs >= 8 chunks per row");
-
-  u32x4 kr[NK];
-  u32x4 vr[NV][2];
-
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ kbase,
-                                       const uint16_t* __restrict__ vbase, size_t row_stride,
-                                       int k0, int kend, int tid) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int c = tid + i * T;
-      const int row = c / CPR, col = c % CPR;
-      const int key = k0 + row;
-      kr[i] = (c < BC * CPR && key < kend)
-                  ? *reinterpret_cast<const u32x4*>(kbase + (size_t)key * row_stride + col * 8)
-                  : zero;
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int pc = tid + i * T;
-      const int j = pc / CPR, col = pc % CPR;
-      const int key = k0 + swap_bits23(2 * j);
-      const bool in = pc < (BC / 2) * CPR;
-      vr[i][0] = (in && key < kend)
-                     ? *reinterpret_cast<const u32x4*>(vbase + (size_t)key * row_stride + col * 8)
-                     : zero;
-      vr[i][1] = (in && key + 1 < kend)
-                     ? *reinterpret_cast<const u32x4*>(vbase + (size_t)(key + 1) * row_stride +
-                                                       col * 8)
-                     : zero;
-    }
-  }
-
-  __device__ __forceinline__ void store(uint16_t* __restrict__ k_lds, uint16_t* __restrict__ vt_lds,
-                                        int tid) const {
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int c = tid + i * T;
-      if (c < BC * CPR) {
-        const int row = c / CPR, col = c % CPR;
-        *reinterpret_cast<u32x4*>(k_lds + row * KSTR + col * 8) = kr[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int pc = tid + i * T;
-      if (pc < (BC / 2) * CPR) {
-        const int j = pc / CPR, col = pc % CPR;
-        uint32_t* vt32 = reinterpret_cast<uint32_t*>(vt_lds);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t a = vr[i][0][e >> 1], b = vr[i][1][e >> 1];
-          const uint32_t pair = (e & 1) ? ((a >> 16) | (b & 0xFFFF0000u))
-                                        : ((a & 0xFFFFu) | (b << 16));
-          const int d = col * 8 + e;
-          const int chunk = (j >> 2) ^ vt_swizzle(d);
-          vt32[d * (BC / 2) + chunk * 4 + (j & 3)] = pair;
-        }
-      }
-    }
-  }
-};
 
 // ---------------------------------------------------------------------------
 // Per-wave attention state and the three steps of one key tile.
@@ -206,25 +111,6 @@ struct WaveState {
     }
   }
 };
-
-// S^T sub-tile: keys kt*32..kt*32+31 of the LDS K tile against the wave's
-// NT query groups.
-template <int D, int NT, int KSTR>
-__device__ __forceinline__ void scores_subtile(f32x16 (&s)[NT], const uint16_t* __restrict__ k_lds,
-                                               int kt, const bf16x8 (&qf)[NT][D / 16], int m32,
-                                               int hh) {
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) s[t][v] = 0.f;
-  const uint16_t* krow = k_lds + (kt * 32 + m32) * KSTR + 8 * hh;
-#pragma unroll
-  for (int st = 0; st < D / 16; ++st) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * st);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) s[t] = mfma_32x32x16(a, qf[t][st], s[t]);
-  }
-}
 
 // Lazy rescaling threshold, in log2 units.  The online-softmax result is exact
 // for any per-row reference value r in place of the running max, as long as
@@ -298,24 +184,6 @@ __device__ __forceinline__ void softmax_update(WaveState<D, NT>& st, f32x16 (&s)
   float alpha[NT];
   const bool moved = softmax_probs<D, NT, NKT>(st, s, pb, alpha, c);
   if (__any(moved)) rescale_o<D, NT>(st, alpha);
-}
-
-// O^T += V^T P^T for keys kt*32..kt*32+31 of the LDS V^T tile (row stride BC).
-template <int D, int NT, int BC>
-__device__ __forceinline__ void pv_subtile(WaveState<D, NT>& st, const uint16_t* __restrict__ vt_lds,
-                                           int kt, const bf16x8 (&pb)[NT][2], int m32, int hh) {
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    const int d = dt * 32 + m32;
-    const int sw = vt_swizzle(d);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int chunk = (kt * 4 + 2 * u + hh) ^ sw;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt_lds + d * BC + chunk * 8);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) st.o[t][dt] = mfma_32x32x16(a, pb[t][u], st.o[t][dt]);
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
