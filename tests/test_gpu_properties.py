@@ -149,3 +149,60 @@ def test_decode_matches_prefill_with_one_query(fa):
                               dev_bf16(v[b:b + 1, :n]), causal=True, out_dtype=torch.float32)
         assert (op[0, 0] - od[b]).abs().max().item() <= 2e-3
         assert (lp[0, 0] - ld[b]).abs().max().item() <= 2e-4
+
+
+def test_one_hot_v_returns_the_probabilities(fa):
+    """V = I (as many keys as head dims) makes O the probability matrix
+    itself: entries >= 0, each row summing to 1, equal to the definition's
+    softmax.  P is rounded to bf16 before the product while l sums the fp32
+    values, so a row sums to 1 within the bf16 relative rounding 2^-9."""
+    import torch
+    import oracle
+    d, nk = 128, 128
+    say("one-hot V")
+    q, k, _ = W.make_fixed(2, 4, 2, nk, nk, d, seed=8, wid=107)  # every row sees a key
+    eye = np.broadcast_to(np.eye(nk, d, dtype=np.float32), (2, 2, nk, d)).transpose(0, 2, 1, 3)
+    v = W.round_f32_to_bf16_bits(np.ascontiguousarray(eye))
+    for causal in (False, True):
+        o, lse = fa.attention(dev_bf16(q), dev_bf16(k), dev_bf16(v), causal=causal,
+                              out_dtype=torch.float32)
+        o = host(o)
+        assert o.min() >= -1e-6
+        assert np.abs(o.sum(-1) - 1.0).max() <= 2.0 ** -9
+        orf, lrf = oracle.attention(q, k, v, 1.0 / np.sqrt(d), causal)
+        assert np.abs(o - orf).max() <= O_TOL
+        assert np.abs(host(lse) - lrf).max() <= LSE_TOL
+
+
+def plain_bf16_attention(q, k, v, scale, causal):
+    """Unfused attention as eager PyTorch computes it on bf16 tensors (on the
+    CPU): S = Q K^T stored as bf16, scaled in bf16, softmax in fp32 stored as
+    bf16, O = P V stored as bf16.  Lq = Lk."""
+    import torch
+    tq, tk, tv = (torch.from_numpy(W.bf16_bits_to_f32(x)).to(torch.bfloat16).transpose(1, 2)
+                  .contiguous() for x in (q, k, v))
+    s = torch.matmul(tq, tk.transpose(-1, -2).contiguous())
+    s = s * torch.tensor(scale, dtype=torch.bfloat16)
+    if causal:
+        n = s.shape[-1]
+        s = s.masked_fill(~torch.ones(n, n, dtype=torch.bool).tril(), float("-inf"))
+    p = torch.softmax(s.float(), dim=-1).to(torch.bfloat16)
+    return torch.matmul(p, tv).transpose(1, 2).float().numpy().astype(np.float64)
+
+
+def test_error_within_twice_a_plain_bf16_attention(fa):
+    """Diagnostic error budget: against the fp64 definition, the fused
+    kernel's bf16 output is no worse than twice the error of plain unfused
+    bf16 attention."""
+    import oracle
+    say("error budget vs plain bf16")
+    bsz, n, h, d = 1, 1024, 4, 128
+    scale = 1.0 / np.sqrt(d)
+    q, k, v = W.make_fixed(bsz, h, h, n, n, d, seed=9, wid=108)
+    for causal in (False, True):
+        og, _ = fa.attention(dev_bf16(q), dev_bf16(k), dev_bf16(v), causal=causal, scale=scale)
+        ref, _ = oracle.attention(q, k, v, scale, causal)
+        err_gpu = np.abs(host(og) - ref).max()
+        err_plain = np.abs(plain_bf16_attention(q, k, v, scale, causal) - ref).max()
+        say("causal", causal, "fused", err_gpu, "plain bf16", err_plain)
+        assert err_gpu <= 2.0 * err_plain
