@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -42,11 +43,21 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def code_without_comments(text: str) -> str:
+    """C/C++ source with comments, trailing blanks and blank lines removed
+    (the sources hold no comment markers inside string literals)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
+def kernel_source_hash(csrc: str = CSRC) -> str:
+    """Hash of the kernel sources' code: a change to the code, not to its
+    comments, makes recorded counter figures stale."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + code_without_comments(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

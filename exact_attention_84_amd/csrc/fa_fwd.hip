@@ -2,20 +2,22 @@
 // variable-length sequences, causal or not, MHA or GQA.
 //
 // Work decomposition: one workgroup per (sequence, query head, tile of BR
-// query rows); the Q tile stays in registers while K/V tiles of BC keys
-// stream through LDS ("FlashAttention — IO 感知的精确注意力 kernel", section
-// 2.3 step 4: one Q tile per thread block, K/V tiles streamed through on-chip
-// memory, launched over (Q blocks, batch, head)).  Causal tiles stop at the
-// diagonal, so a causal forward does about half the work ("推理优化 |
-// FlashAttention 1-4 详解", section FlashAttention 2 的工程优化, causal
-// lower-triangle skipping).  Masks are applied only on tiles that cross the
-// diagonal or the end of the keys.
+// query rows) -- causal: a pair of tiles, n-1-i and i, of the same sequence;
+// the Q tile stays in registers while K/V tiles of BC keys stream through LDS
+// ("FlashAttention — IO 感知的精确注意力 kernel", section 2.3 step 4: one Q
+// tile per thread block, K/V tiles streamed through on-chip memory, launched
+// over (Q blocks, batch, head)).  Causal tiles stop at the diagonal, so a
+// causal forward does about half the work ("推理优化 | FlashAttention 1-4
+// 详解", section FlashAttention 2 的工程优化, causal lower-triangle
+// skipping).  Masks are applied only on tiles that cross the diagonal or the
+// end of the keys.
 //
 // Within a wave the key loop is software-pipelined so that the matrix core and
 // the ALUs work at the same time (the GEMM/softmax overlap of the first page's
 // FlashAttention 3 notes, section FlashAttention 3 的硬件特性利用, done here
-// inside one wavefront): step j issues the score MFMAs of tile j+1 and the
-// P V MFMAs of tile j-1, and runs the softmax of tile j between them.
+// inside one wavefront): step j computes the scores of tile j, then issues the
+// P V MFMAs of tile j-1 one by one with a slice of the softmax of tile j after
+// each.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -139,7 +141,8 @@ __device__ __forceinline__ bool steady_step(WaveState<D, NT>& st, const char* __
 }
 
 // Two waves per SIMD (256 registers each) when a wave owns 32 query rows, so
-// that one wave's MFMAs overlap the other's softmax arithmetic.
+// that one wave's MFMAs overlap the other's softmax arithmetic.  NW is 4 or 8
+// (fwd_waves); PAIR runs two causal query tiles per workgroup.
 template <int D, int NW, int NT, bool CAUSAL, bool PAIR>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
 void fwd_kernel(const FwdParams p) {

@@ -84,3 +84,14 @@ def test_cpu_baseline_reports_its_sample():
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
     assert r["value"] > 0 and r["cores"] >= 1
     assert "single_head_n256_d64" in r["sample"]
+
+
+def test_source_hash_ignores_comments_only(tmp_path):
+    src = tmp_path / "csrc"
+    src.mkdir()
+    (src / "k.hip").write_text("// header\nint f(int x) {  // doubled\n  return 2 * x;\n}\n")
+    h0 = bench.kernel_source_hash(str(src))
+    (src / "k.hip").write_text("/* new\n   header */\n\nint f(int x) {\n  return 2 * x;  // twice\n}\n")
+    assert bench.kernel_source_hash(str(src)) == h0
+    (src / "k.hip").write_text("int f(int x) {\n  return 3 * x;\n}\n")
+    assert bench.kernel_source_hash(str(src)) != h0
