@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the exact attention forward (test infrastructure only).
+"""fp64 CPU oracle for exact attention and its gradients (test infrastructure
+only).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  It shares no code with the HIP library.
@@ -17,4 +18,9 @@ from .exact import (  # noqa: F401
     softmax_rows,
     tiled_online_attention,
     to_f64,
+)
+from .grad import (  # noqa: F401
+    attention_grad,
+    attention_grad_varlen,
+    head_attention_grad,
 )
