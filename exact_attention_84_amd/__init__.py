@@ -109,6 +109,69 @@ def attention(q, k, v, *, causal: bool = False, scale: float | None = None,
     return out, lse
 
 
+def attention_backward(q, k, v, out, lse, dout, *, causal: bool = False,
+                       scale: float | None = None, cu_seqlens_q=None, cu_seqlens_k=None,
+                       max_seqlen_q: int | None = None, max_seqlen_k: int | None = None,
+                       grad_dtype=torch.float32, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of <dout, out> for ``attention``'s forward, given
+    its output and logsumexp.  Shapes and conventions as ``attention``;
+    dout has out's shape and dtype bf16.  ``workspace`` (uint8 device tensor)
+    is allocated when omitted."""
+    lib = load()
+    varlen = cu_seqlens_q is not None
+    ndim = 3 if varlen else 4
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _need(t, n, torch.bfloat16, ndim)
+    _need(lse, "lse", torch.float32)
+    if grad_dtype not in _OUT_DTYPES:
+        raise TypeError("grad_dtype must be torch.bfloat16 or torch.float32")
+    if k.shape != v.shape or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("k/v and q/out/dout shapes must match")
+    d = q.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if varlen:
+        _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+        if cu_seqlens_k is not None:
+            _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+        batch = cu_seqlens_q.numel() - 1
+        if max_seqlen_q is None:
+            max_seqlen_q = int(torch.diff(cu_seqlens_q).max().item()) if batch > 0 else 0
+        if max_seqlen_k is None:
+            ck = cu_seqlens_q if cu_seqlens_k is None else cu_seqlens_k
+            max_seqlen_k = int(torch.diff(ck).max().item()) if batch > 0 else 0
+        hq, hkv = q.shape[1], k.shape[1]
+        nq, nk = 0, 0
+        rows_q = max_seqlen_q
+        lse_shape = (q.shape[0], hq)
+    else:
+        batch, nq, hq, _ = q.shape
+        nk, hkv = k.shape[1], k.shape[2]
+        max_seqlen_q = max_seqlen_k = 0
+        rows_q = nq
+        lse_shape = (batch, nq, hq)
+    if tuple(lse.shape) != lse_shape:
+        raise ValueError(f"lse must have shape {lse_shape}")
+    need = lib.fa_bwd_workspace_size(batch, hq, rows_q)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _need(workspace, "workspace", torch.uint8)
+    dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
+    dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device)
+    dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
+    st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq),
+                    _ptr(dk), _ptr(dv), batch, hq, hkv, nq, nk, d, scale, int(bool(causal)),
+                    _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), int(max_seqlen_q), int(max_seqlen_k),
+                    _OUT_DTYPES[grad_dtype], _ptr(workspace), workspace.numel(),
+                    _stream_handle(stream))
+    check(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def bwd_workspace_size(batch: int, heads_q: int, max_seqlen_q: int) -> int:
+    return int(load().fa_bwd_workspace_size(batch, heads_q, max_seqlen_q))
+
+
 def decode_workspace_size(batch: int, heads_q: int, max_cache_len: int, head_dim: int,
                           chunk: int = 0) -> int:
     return int(load().fa_decode_workspace_size(batch, heads_q, max_cache_len, head_dim, chunk))

@@ -19,7 +19,7 @@ STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD
                 4: "FA_ERR_GQA", 5: "FA_ERR_DTYPE", 6: "FA_ERR_ARCH", 7: "FA_ERR_WORKSPACE",
                 8: "FA_ERR_HIP", 9: "FA_ERR_ARG"}
 EXPORTS = ("fa_fwd", "fa_decode_workspace_size", "fa_fwd_decode_splitkv", "fa_combine",
-           "fa_status_string", "fa_last_error")
+           "fa_bwd_workspace_size", "fa_bwd", "fa_status_string", "fa_last_error")
 
 _lib = None
 
@@ -53,6 +53,11 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_decode_splitkv.restype = I
     lib.fa_combine.argtypes = [P, P, I, I, I, P, P, I, P]
     lib.fa_combine.restype = I
+    lib.fa_bwd_workspace_size.argtypes = [I, I, I]
+    lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, I, I, I, P,
+                           ctypes.c_size_t, P]
+    lib.fa_bwd.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []

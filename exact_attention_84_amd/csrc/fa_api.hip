@@ -272,4 +272,94 @@ fa_status fa_combine(const float* o_part, const float* lse_part, int rows, int n
   return ok();
 }
 
+size_t fa_bwd_workspace_size(int batch, int heads_q, int max_seqlen_q) {
+  if (batch < 0 || heads_q <= 0 || max_seqlen_q < 0) return 0;
+  const long long rows = (long long)batch * max_seqlen_q;
+  if (rows > kMaxElems) return 0;
+  return 2 * (size_t)heads_q * (size_t)(rows + fa::kBwdPad) * sizeof(float);
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int batch, int heads_q,
+                 int heads_kv, int seqlen_q, int seqlen_k, int head_dim, float scale, int causal,
+                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int max_seqlen_q,
+                 int max_seqlen_k, fa_dtype grad_dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  if (!valid_head_dim(head_dim))
+    return fail(FA_ERR_HEADDIM, "head_dim %d not supported (64 or 128)", head_dim);
+  if (batch < 0 || heads_q <= 0 || heads_kv <= 0)
+    return fail(FA_ERR_SHAPE, "batch >= 0 and heads > 0 required (batch %d, heads %d/%d)", batch,
+                heads_q, heads_kv);
+  if (heads_q % heads_kv)
+    return fail(FA_ERR_GQA, "heads_kv %d does not divide heads_q %d", heads_kv, heads_q);
+  if (!valid_scale(scale)) return fail(FA_ERR_ARG, "scale must be finite and > 0");
+  if (causal != 0 && causal != 1) return fail(FA_ERR_ARG, "causal must be 0 or 1");
+  if (grad_dtype != FA_DTYPE_BF16 && grad_dtype != FA_DTYPE_F32)
+    return fail(FA_ERR_DTYPE, "grad_dtype %d unknown", (int)grad_dtype);
+  const bool varlen = cu_seqlens_q != nullptr;
+  int rows_q, rows_k;
+  if (varlen) {
+    if (max_seqlen_q < 0 || max_seqlen_k < 0)
+      return fail(FA_ERR_SHAPE, "max_seqlen_q/k must be >= 0");
+    rows_q = max_seqlen_q;
+    rows_k = max_seqlen_k;
+  } else {
+    if (seqlen_q < 0 || seqlen_k < 0) return fail(FA_ERR_SHAPE, "seqlen_q/k must be >= 0");
+    rows_q = seqlen_q;
+    rows_k = seqlen_k;
+  }
+  const long long nq = (long long)batch * rows_q, nk = (long long)batch * rows_k;
+  if (nq * heads_q * head_dim > kMaxElems || nk * heads_kv * head_dim > kMaxElems)
+    return fail(FA_ERR_SHAPE, "tensor too large");
+  if ((!q || !o || !dout || !lse || !dq) && nq > 0)
+    return fail(FA_ERR_NULL, "q, o, dout, lse and dq must be non-NULL");
+  if ((!k || !v || !dk || !dv) && nk > 0)
+    return fail(FA_ERR_NULL, "k, v, dk and dv must be non-NULL");
+  const int bq = fa::bwd_dq_rows(), bk = fa::bwd_dkdv_keys();
+  const long long n_qtiles = (rows_q + bq - 1) / bq;
+  const long long n_kblocks = (rows_k + bk - 1) / bk;
+  if ((long long)batch * heads_q * n_qtiles > 0x7fffffffLL ||
+      (long long)batch * heads_kv * n_kblocks > 0x7fffffffLL || nq * heads_q > 0x7fffffffLL)
+    return fail(FA_ERR_SHAPE, "too many tiles");
+  if (nq == 0 && nk == 0) return ok();  // nothing to compute
+  const size_t need = fa_bwd_workspace_size(batch, heads_q, rows_q);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 3))
+    return fail(FA_ERR_WORKSPACE, "workspace needs %zu bytes, 4-byte aligned (got %zu)", need,
+                workspace_bytes);
+
+  fa_status s = check_device();
+  if (s != FA_OK) return s;
+
+  fa::BwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.rows_cap = (int)nq;
+  p.ws_stride = p.rows_cap + fa::kBwdPad;
+  p.dsum = static_cast<float*>(workspace);
+  p.lse2 = p.dsum + (size_t)heads_q * p.ws_stride;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = varlen ? (cu_seqlens_k ? cu_seqlens_k : cu_seqlens_q) : nullptr;
+  p.batch = batch;
+  p.hq = heads_q;
+  p.hkv = heads_kv;
+  p.group = heads_q / heads_kv;
+  p.seqlen_q = seqlen_q;
+  p.seqlen_k = seqlen_k;
+  p.n_qtiles = (int)n_qtiles;
+  p.n_kblocks = (int)n_kblocks;
+  p.scale = scale;
+  p.c = scale * fa::kLog2eHost;
+  p.g_f32 = grad_dtype == FA_DTYPE_F32;
+  hipError_t e = fa::launch_bwd(p, head_dim, causal != 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

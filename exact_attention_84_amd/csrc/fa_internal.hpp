@@ -59,6 +59,40 @@ struct DecodeParams {
 // query) for fixed-length batches of at least 2048 queries at head_dim 128,
 // else 4 (128 rows; less padding and more workgroups for short or packed
 // sequences).
+// Backward.  The workspace holds two fp32 arrays [Hq][rows_cap + pad]:
+// D = rowsum(dO * O) and LSE * log2(e), head-major so that a lane can read
+// four consecutive query rows at once.
+constexpr int kBwdPad = 64;  // rows of padding after each head's rows
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;       // [rows, Hq], natural log
+  float* dsum;            // workspace: D [Hq][rows_cap + kBwdPad]
+  float* lse2;            // workspace: LSE * log2(e), same layout
+  void* dq;               // [rows, Hq, d]
+  void* dk;               // [key rows, Hkv, d]
+  void* dv;
+  const int32_t* cu_q;    // NULL: fixed-length batch
+  const int32_t* cu_k;
+  int batch, hq, hkv, group;
+  int seqlen_q, seqlen_k;  // fixed-length mode
+  int rows_cap;           // batch * (seqlen_q or max_seqlen_q): bound on query rows
+  int ws_stride;          // rows_cap + kBwdPad
+  int n_qtiles;           // dQ kernel: query tiles per (sequence, head), longest sequence
+  int n_kblocks;          // dK/dV kernel: key blocks per (sequence, kv head), longest
+  float scale;
+  float c;                // scale * log2(e)
+  int g_f32;              // gradients stored as fp32 (else bf16)
+};
+
+int bwd_dq_rows();       // query rows per dQ workgroup
+int bwd_dkdv_keys();     // keys per dK/dV workgroup
+hipError_t launch_bwd(const BwdParams& p, int head_dim, bool causal, hipStream_t stream);
+
 int fwd_waves(int head_dim, bool varlen, int seqlen_q);
 int fwd_block_rows(int waves);
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, hipStream_t stream);

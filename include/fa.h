@@ -147,6 +147,45 @@ fa_status fa_fwd_decode_splitkv(const void* q, const void* k_cache, const void* 
 fa_status fa_combine(const float* o_part, const float* lse_part, int rows, int n_splits,
                      int head_dim, void* o, float* lse, fa_dtype o_dtype, void* stream);
 
+/*
+ * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs: two fp32
+ * arrays (rowsum(dO * O) and the logsumexp in base 2) of heads_q x
+ * (batch * max_seqlen_q + 64) values.  For a fixed-length batch pass
+ * max_seqlen_q = seqlen_q.  Returns 0 for invalid sizes.
+ */
+size_t fa_bwd_workspace_size(int batch, int heads_q, int max_seqlen_q);
+
+/*
+ * fa_bwd -- gradients of the scalar <dout, o> with respect to q, k and v for
+ * the forward of fa_fwd (same shapes, layouts, scale, causal rule and varlen
+ * conventions).  The backward keeps only o and lse from the forward and
+ * recomputes P = exp(S scale - lse) tile by tile ("FlashAttention — IO 感知
+ * 的精确注意力 kernel", section 4: the backward recomputes P from the saved
+ * logsumexp and is split by key blocks; section 2.3: autograd saves q, k, v,
+ * out and the logsumexp).  With D = rowsum(dout * o):
+ *   dv = P^T dout,  dS = P * (dout v^T - D),  dq = scale dS k,
+ *   dk = scale dS^T q;
+ * a kv head receives the sum over the query heads of its group.
+ *
+ *   q, o, dout, dq : as q in fa_fwd;   k, v, dk, dv : as k in fa_fwd
+ *   lse            : float32, the forward's natural-log logsumexp
+ *   dq, dk, dv     : written in grad_dtype (bf16 or fp32); every row of the
+ *                    batch is written, keys no query sees get zero.
+ *   workspace      : device memory of at least fa_bwd_workspace_size(batch,
+ *                    heads_q, varlen ? max_seqlen_q : seqlen_q) bytes,
+ *                    4-byte aligned; contents on entry are ignored.
+ *   varlen         : max_seqlen_q / max_seqlen_k must bound every sequence.
+ * Bitwise deterministic: dq is computed by its own pass, not by atomic adds.
+ * Enqueues three kernels on `stream`.  Errors as fa_fwd, plus
+ * FA_ERR_WORKSPACE for a missing, short or misaligned workspace.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int batch, int heads_q,
+                 int heads_kv, int seqlen_q, int seqlen_k, int head_dim, float scale, int causal,
+                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int max_seqlen_q,
+                 int max_seqlen_k, fa_dtype grad_dtype, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(fa_status status);
 

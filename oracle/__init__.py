@@ -23,4 +23,7 @@ from .grad import (  # noqa: F401
     attention_grad,
     attention_grad_varlen,
     head_attention_grad,
+    prob_grad,
+    probabilities,
+    softmax_backward,
 )

@@ -31,7 +31,7 @@ import math
 import numpy as np
 
 # Tensor ids inside a workload's seed sequence.
-T_Q, T_K, T_V, T_LEN = 0, 1, 2, 3
+T_Q, T_K, T_V, T_LEN, T_DO = 0, 1, 2, 3, 4
 
 
 @dataclasses.dataclass(frozen=True)
@@ -134,6 +134,20 @@ def make_varlen(lengths_q, lengths_k, heads_q, heads_kv, head_dim, *, seed=0, wi
                                              s, k_mult)
         v[cu_k[s]:cu_k[s + 1]] = normal_bf16(seed, wid, T_V, (lengths_k[s], heads_kv, head_dim), s)
     return q, k, v, cu_q, cu_k
+
+
+def make_dout(q_shape, *, seed=0, wid=0, cu_q=None) -> np.ndarray:
+    """Upstream gradient dO with the query tensor's shape (bf16 bits): one
+    slice per batch entry, or per packed sequence when ``cu_q`` is given."""
+    do = np.empty(q_shape, np.uint16)
+    if cu_q is None:
+        for b in range(q_shape[0]):
+            do[b] = normal_bf16(seed, wid, T_DO, q_shape[1:], b)
+    else:
+        for s in range(len(cu_q) - 1):
+            a, e = int(cu_q[s]), int(cu_q[s + 1])
+            do[a:e] = normal_bf16(seed, wid, T_DO, (e - a,) + tuple(q_shape[1:]), s)
+    return do
 
 
 BF16_NAN = np.uint16(0x7FC0)
