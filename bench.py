@@ -51,28 +51,60 @@ def code_without_comments(text: str) -> str:
     return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
 
 
-def kernel_source_hash(csrc: str = CSRC) -> str:
-    """Hash of the kernel sources' code: a change to the code, not to its
-    comments, makes recorded counter figures stale."""
+def unit_files(unit: str, csrc: str = CSRC) -> list:
+    """The files a kernel's code comes from: its translation unit, the host
+    code that fills its parameters (fa_api.hip, when present), and every
+    local header they include, recursively."""
+    todo = [unit] + (["fa_api.hip"] if os.path.exists(os.path.join(csrc, "fa_api.hip")) else [])
+    seen = []
+    while todo:
+        f = todo.pop()
+        if f in seen or not os.path.exists(os.path.join(csrc, f)):
+            continue
+        seen.append(f)
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            todo += re.findall(r'^\s*#\s*include\s+"([^"]+)"', fh.read(), re.M)
+    return sorted(seen)
+
+
+def kernel_source_hash(unit: str = "fa_fwd.hip", csrc: str = CSRC) -> str:
+    """Hash of the code a kernel is built from (its unit's files, comments
+    removed) and of the unit's compiler options: a change to either, not to
+    comments, makes recorded counter figures for that kernel stale."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
+    for f in unit_files(unit, csrc):
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             h.update(f.encode() + code_without_comments(fh.read()).encode())
+    try:
+        from exact_attention_84_amd import build as B
+        h.update(" ".join(B.flags() + B.SOURCE_FLAGS.get(unit, [])).encode())
+    except ImportError:  # pragma: no cover
+        pass
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources; else None."""
+# kernel-name pattern -> (traffic.json tag, translation unit)
+TRAFFIC_KERNELS = {
+    "fwd_kernel<128, 8, 1, false, false>": ("fwd_noncausal_d128", "fa_fwd.hip"),
+    "fwd_kernel<128, 8, 1, true, true>": ("fwd_causal_d128", "fa_fwd.hip"),
+    "decode_kernel<128>": ("decode_d128", "fa_decode.hip"),
+    "bwd_dkdv_kernel<128, 4, false>": ("bwd_dkdv_noncausal_d128", "fa_bwd.hip"),
+    "bwd_dq_kernel<128, 4, false>": ("bwd_dq_noncausal_d128", "fa_bwd.hip"),
+}
+
+
+def measured_traffic(tag: str):
+    """HBM bytes per launch of one kernel from committed rocprofv3 counter
+    runs, if they were taken on that kernel's current sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != kernel_source_hash():
+    k = t.get("kernels", {}).get(tag)
+    if k is None or k.get("source_hash") != kernel_source_hash(k.get("unit", "")):
         return None
-    k = t.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("bytes_per_launch")
+    return k.get("bytes_per_launch")
 
 
 def write_traffic(fetch_dir: str, write_dir: str) -> dict:
@@ -92,7 +124,7 @@ def write_traffic(fetch_dir: str, write_dir: str) -> dict:
         return vals
 
     copy_bytes = float(1 << 30)
-    out = {"source_hash": kernel_source_hash(), "kernels": {}, "scale": {}}
+    out = {"kernels": {}, "scale": {}}
     per = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals = per_kernel(d, counter)
@@ -106,14 +138,13 @@ def write_traffic(fetch_dir: str, write_dir: str) -> dict:
         out["scale"][counter] = round(factor, 4)
         for k, v in kib.items():
             per.setdefault(k, {})[counter] = v * 1024.0 * factor
-    names = {"fwd_kernel<128, 8, 1, false, false>": "fwd_noncausal_d128",
-             "fwd_kernel<128, 8, 1, true, true>": "fwd_causal_d128",
-             "decode_kernel<128>": "decode_d128"}
     for k, v in per.items():
-        for pat, tag in names.items():
+        for pat, (tag, unit) in TRAFFIC_KERNELS.items():
             if pat in k and "FETCH_SIZE" in v and "WRITE_SIZE" in v:
                 rd, wr = round(v["FETCH_SIZE"]), round(v["WRITE_SIZE"])
-                out["kernels"][tag] = {"kernel": k, "read_bytes": rd, "write_bytes": wr,
+                out["kernels"][tag] = {"kernel": k, "unit": unit,
+                                       "source_hash": kernel_source_hash(unit),
+                                       "read_bytes": rd, "write_bytes": wr,
                                        "bytes_per_launch": rd + wr}
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -195,6 +226,34 @@ def other_workloads(fa, steps, warmup):
     return res
 
 
+def backward_workload(fa, w, steps, warmup):
+    """The attention backward (preprocess, dK/dV and dQ kernels) on the
+    headline workload, non-causal and causal, from the forward's own O and
+    LSE.  Algorithmic flops: the five products S, dP, dV, dK, dQ of
+    2 N_q N_k d each per head, 2.5 times the forward's (halved when causal)."""
+    import torch
+    inp = W.make_workload(w, seed=0)
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    do = to_dev(W.make_dout(inp["q"].shape, seed=0, wid=w.wid))
+    ws = torch.empty(fa.bwd_workspace_size(w.batch, w.heads_q, w.seqlen_q), dtype=torch.uint8,
+                     device="cuda")
+    res = {}
+    for causal in (False, True):
+        o, lse = fa.attention(q, k, v, causal=causal, scale=w.scale)
+        ms = time_calls(lambda: fa.attention_backward(q, k, v, o, lse, do, causal=causal,
+                                                      scale=w.scale, workspace=ws,
+                                                      grad_dtype=torch.bfloat16),
+                        steps, warmup)
+        fl = 2.5 * W.flops(w, causal=causal)
+        tf = fl / (ms * 1e-3) / 1e12
+        res["causal" if causal else "noncausal"] = {
+            "ms": round(ms, 4), "tflops": round(tf, 1),
+            "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "gflop": round(fl / 1e9, 1)}
+        log("backward", w.name, "causal" if causal else "non-causal", res[
+            "causal" if causal else "noncausal"])
+    return res
+
+
 def cold_launches(fn, n, flush):
     """Average event-timed duration of `fn` when each launch follows a write
     of `flush` (512 MiB, twice the 256 MB last-level cache), so that its
@@ -234,7 +293,8 @@ def decode_inputs(fa, w):
 
 def probe(fa, w, steps, warmup):
     """Launches for rocprofv3 counter runs: the headline workload's non-causal
-    and causal forward, the split-KV decode workload, then a 1 GiB
+    and causal forward, the split-KV decode workload, the headline workload's
+    non-causal backward (bf16 gradients), then a 1 GiB
     device-to-device copy (a kernel that reads and writes exactly 1 GiB each,
     to scale the byte counters)."""
     import torch
@@ -251,12 +311,21 @@ def probe(fa, w, steps, warmup):
     for _ in range(warmup + steps):
         fa.decode(*args, scale=wd.scale, **kw)
     del args, kw
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    do = to_dev(W.make_dout(inp["q"].shape, seed=0, wid=w.wid))
+    o, lse = fa.attention(q, k, v, causal=False, scale=w.scale)
+    ws = torch.empty(fa.bwd_workspace_size(w.batch, w.heads_q, w.seqlen_q), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(warmup + steps):
+        fa.attention_backward(q, k, v, o, lse, do, causal=False, scale=w.scale, workspace=ws,
+                              grad_dtype=torch.bfloat16)
+    del q, k, v, do, o, lse, ws
     a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
     for _ in range(steps):
         b.copy_(a)
     torch.cuda.synchronize()
-    log(f"probe: {warmup + steps} non-causal, causal and decode launches, "
+    log(f"probe: {warmup + steps} non-causal, causal, decode and backward launches, "
         f"{steps} copies of {a.numel() * 4} bytes")
 
 
@@ -408,6 +477,9 @@ def main():
     del o_nc, o_c, lse_nc, lse_c
     if not a.no_extra:
         res["other_workloads"] = other_workloads(fa, max(5, a.steps // 5), max(3, a.warmup // 5))
+        res["backward"] = {"workload": w.name, "grad_dtype": "bf16",
+                           **backward_workload(fa, w, max(5, a.steps // 5),
+                                               max(3, a.warmup // 5))}
     if not a.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w)
         log("cpu_baseline", res["cpu_baseline"])

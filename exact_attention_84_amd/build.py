@@ -20,6 +20,11 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip"]
+# Per-source code-generation options.  The dK/dV kernel runs one wave per
+# SIMD with its accumulators live across the whole loop; selecting the VGPR
+# form of the MFMA instructions keeps them in place instead of copying them
+# between AGPRs and VGPRs around every product.
+SOURCE_FLAGS = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 
@@ -40,7 +45,8 @@ def flags(defines=()):
 
 
 def _compile(src, out, defines):
-    cmd = [hipcc(), *flags(defines), "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [hipcc(), *flags(defines), *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+           "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in (r.stderr or "").splitlines()
                     if "packed-fp32-ops" not in l)

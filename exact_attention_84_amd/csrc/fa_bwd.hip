@@ -30,6 +30,10 @@
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
+#ifndef FA_DKDV_WPE
+#define FA_DKDV_WPE 1
+#endif
+
 namespace fa {
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
@@ -233,10 +237,12 @@ void bwd_dq_kernel(const BwdParams p) {
 // dK, dV: each wave owns 32 keys (one per lane column).  Per 32-query
 // sub-tile of the streamed Q / dO tiles it forms S = Q K^T and dP = dO V^T
 // (rows = queries), P and dS in registers with the query rows' LSE and D,
-// then dV^T += dO^T P and dK^T += Q^T dS.
+// then dV^T += dO^T P and dK^T += Q^T dS.  The rows' LSE log2(e) and D ride
+// along with each Q / dO tile into LDS, so the inner loop reads no global
+// memory.
 // ---------------------------------------------------------------------------
 template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DKDV_WPE)))
 void bwd_dkdv_kernel(const BwdParams p) {
   constexpr int BQ = 64;
   constexpr int BK = NW * 32;
@@ -246,6 +252,9 @@ void bwd_dkdv_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char q_lds1[TILE];
   __shared__ __attribute__((aligned(1024))) char do_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) char do_lds1[TILE];
+  // per stage: LSE log2(e) of the tile's 64 rows, then their D (the DMA
+  // instruction fills 1 KB; the second half repeats the first)
+  __shared__ __attribute__((aligned(1024))) float st_lds[2][256];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -274,13 +283,18 @@ void bwd_dkdv_kernel(const BwdParams p) {
   const int k0 = kblk * BK;
   if (k0 >= Lk) return;  // packed sequence shorter than this block (uniform)
   const int delta = Lk - Lq;
+  // rows at or past this bound have no workspace entry (a launch sized for
+  // fewer rows than the sequences hold); they are masked like padding
+  const int lq_eff = min(Lq, p.rows_cap - q_start);
   const int kw0 = k0 + wave * 32;
   const int key = kw0 + m32;
   const bool key_ok = key < Lk;
 
   const size_t q_stride = (size_t)p.hq * D;
   const size_t kv_stride = (size_t)p.hkv * D;
-  bf16x8 kf[1][KS], vf[1][KS];  // this lane's key row of K and V
+  // this lane's key row of K and V (zeros past the end: their gradients are
+  // accumulated but never stored)
+  bf16x8 kf[1][KS], vf[1][KS];
   {
     const size_t off = (size_t)(k_start + key) * kv_stride + (size_t)kvh * D + 8 * hh;
 #pragma unroll
@@ -309,49 +323,63 @@ void bwd_dkdv_kernel(const BwdParams p) {
   dma.init(q_stride, wave, lane);
   LdsRead<D> rd;
   rd.init(lane);
-  auto issue = [&](int step, char* ql, char* dol) {
-    const int hg = step / per_head, qt = qt0 + step % per_head;
-    const size_t head = (size_t)(p.group * kvh + hg) * D;
+  auto issue = [&](int step, int stage) {
+    const int hg = step / per_head, q0 = (qt0 + step % per_head) * BQ;
+    const int h = p.group * kvh + hg;
+    const size_t head = (size_t)h * D;
     const uint16_t* qb = p.q + (size_t)q_start * q_stride + head;
     const uint16_t* db = p.dout + (size_t)q_start * q_stride + head;
-    dma.issue(qb, q_stride, qt * BQ, Lq - 1, ql, wave, lane);
-    dma.issue(db, q_stride, qt * BQ, Lq - 1, dol, wave, lane);
+    dma.issue(qb, q_stride, q0, Lq - 1, stage ? q_lds1 : q_lds0, wave, lane);
+    dma.issue(db, q_stride, q0, Lq - 1, stage ? do_lds1 : do_lds0, wave, lane);
+    if (wave == 0) {
+      // 16 lanes x 16 bytes per statistic; the row base is clamped so the
+      // 64-row read stays inside the workspace (its 64 rows of padding)
+      const int r0 = min(q_start + q0, p.ws_stride - BQ);
+      const float* src = ((lane & 16) ? p.dsum : p.lse2) + (size_t)h * p.ws_stride + r0 +
+                         4 * (lane & 15);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)st_lds[stage], 16, 0, 0);
+    }
   };
-  if (n_steps > 0) issue(0, q_lds0, do_lds0);
+  if (n_steps > 0) issue(0, 0);
 
 #pragma clang loop unroll(disable)
   for (int step = 0; step < n_steps; ++step) {
-    const char* qc = (step & 1) ? q_lds1 : q_lds0;
-    const char* dc = (step & 1) ? do_lds1 : do_lds0;
+    const int stage = step & 1;
+    const char* qc = stage ? q_lds1 : q_lds0;
+    const char* dc = stage ? do_lds1 : do_lds0;
+    const float* stl = st_lds[stage];
     wait_dma();
     __syncthreads();  // this tile has landed; everyone is done with the other stage
-    if (step + 1 < n_steps)
-      issue(step + 1, (step & 1) ? q_lds0 : q_lds1, (step & 1) ? do_lds0 : do_lds1);
+    if (step + 1 < n_steps) issue(step + 1, stage ^ 1);
     if (kw0 >= Lk) continue;  // this wave has no keys (uniform)
-    const int h = p.group * kvh + step / per_head;
     const int q0 = (qt0 + step % per_head) * BQ;
-    const float* l2 = p.lse2 + (size_t)h * p.ws_stride;
-    const float* dsm = p.dsum + (size_t)h * p.ws_stride;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int qsub = q0 + 32 * kt;
-      if (qsub >= Lq) break;                             // past the queries (uniform)
-      if (CAUSAL && kw0 > qsub + 31 + delta) continue;   // every key above the diagonal
+      if (qsub >= Lq) break;                            // past the queries (uniform)
+      if (CAUSAL && kw0 > qsub + 31 + delta) continue;  // every key above the diagonal
       f32x16 s[1][1], dp[1][1];
       scores_tile<D, 1, 1>(s, qc + kt * 64 * D, rd, kf);   // S = Q K^T
       scores_tile<D, 1, 1>(dp, dc + kt * 64 * D, rd, vf);  // dP = dO V^T
+      // the lane's rows are qsub + 8 g + 4 hh + 0..3 for register group g
+      const bool full = qsub + 31 < lq_eff && (!CAUSAL || kw0 + 31 <= qsub + delta);
+      const int lo = key - delta - qsub - 4 * hh;  // first admissible row offset (causal)
+      const int hi = lq_eff - 1 - qsub - 4 * hh;   // last row offset with data
       float pe[16], ds[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = qsub + acc_row(v, hh);
-        const bool ok = key_ok && row < Lq && q_start + row < p.rows_cap &&
-                        (!CAUSAL || key <= row + delta);
-        // rows past Lq read the workspace padding (index clamped to the
-        // buffer); the select drops them
-        const int wi = min(q_start + row, p.ws_stride - 1);
-        const float lr = l2[wi], dr = dsm[wi];
-        pe[v] = ok ? fast_exp2(fmaf(s[0][0][v], p.c, -lr)) : 0.f;
-        ds[v] = ok ? pe[v] * (dp[0][0][v] - dr) : 0.f;
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(stl + 32 * kt + 8 * g + 4 * hh);
+        const f32x4 dd = *reinterpret_cast<const f32x4*>(stl + 64 + 32 * kt + 8 * g + 4 * hh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = 4 * g + e;
+          const float pv = fast_exp2(fmaf(s[0][0][v], p.c, -l2[e]));
+          const float dv = pv * (dp[0][0][v] - dd[e]);
+          const int r = 8 * g + e;
+          const bool ok = full || (r <= hi && (!CAUSAL || r >= lo));
+          pe[v] = ok ? pv : 0.f;
+          ds[v] = ok ? dv : 0.f;
+        }
       }
       bf16x8 pb[1][1][2], dsb[1][1][2];
       pb[0][0][0] = pack_bf16x8(pe);

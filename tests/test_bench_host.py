@@ -56,11 +56,14 @@ def test_write_traffic_scales_by_the_copy_kernel(tmp_path, monkeypatch):
     assert k["bytes_per_launch"] == k["read_bytes"] + k["write_bytes"]
     assert t["kernels"]["fwd_causal_d128"]["read_bytes"] == 500 * 1024 * 2
     assert json.loads(out_file.read_text()) == t
-    # read back only while the kernel sources are unchanged
+    assert k["unit"] == "fa_fwd.hip" and k["source_hash"] == bench.kernel_source_hash("fa_fwd.hip")
+    # read back only while the kernel's sources are unchanged
     assert bench.measured_traffic("fwd_noncausal_d128") == k["bytes_per_launch"]
-    stale = dict(t, source_hash="0" * 16)
+    stale = json.loads(json.dumps(t))
+    stale["kernels"]["fwd_noncausal_d128"]["source_hash"] = "0" * 16
     out_file.write_text(json.dumps(stale))
     assert bench.measured_traffic("fwd_noncausal_d128") is None
+    assert bench.measured_traffic("fwd_causal_d128") is not None
 
 
 def test_write_traffic_needs_the_copy_kernel(tmp_path, monkeypatch):
@@ -74,8 +77,8 @@ def test_write_traffic_needs_the_copy_kernel(tmp_path, monkeypatch):
 def test_committed_traffic_file_is_well_formed():
     with open(bench.TRAFFIC_FILE) as fh:
         t = json.load(fh)
-    assert len(t["source_hash"]) == 16
     for k in t["kernels"].values():
+        assert len(k["source_hash"]) == 16 and k["unit"].endswith(".hip")
         assert k["bytes_per_launch"] == k["read_bytes"] + k["write_bytes"] > 0
 
 
@@ -90,8 +93,23 @@ def test_source_hash_ignores_comments_only(tmp_path):
     src = tmp_path / "csrc"
     src.mkdir()
     (src / "k.hip").write_text("// header\nint f(int x) {  // doubled\n  return 2 * x;\n}\n")
-    h0 = bench.kernel_source_hash(str(src))
+    h0 = bench.kernel_source_hash("k.hip", str(src))
     (src / "k.hip").write_text("/* new\n   header */\n\nint f(int x) {\n  return 2 * x;  // twice\n}\n")
-    assert bench.kernel_source_hash(str(src)) == h0
+    assert bench.kernel_source_hash("k.hip", str(src)) == h0
     (src / "k.hip").write_text("int f(int x) {\n  return 3 * x;\n}\n")
-    assert bench.kernel_source_hash(str(src)) != h0
+    assert bench.kernel_source_hash("k.hip", str(src)) != h0
+
+
+def test_source_hash_covers_the_unit_and_its_headers_only(tmp_path):
+    src = tmp_path / "csrc"
+    src.mkdir()
+    (src / "a.hpp").write_text("int g();\n")
+    (src / "b.hpp").write_text('#include "a.hpp"\n')
+    (src / "k.hip").write_text('#include "b.hpp"\nint f();\n')
+    (src / "other.hip").write_text("int h();\n")
+    assert bench.unit_files("k.hip", str(src)) == ["a.hpp", "b.hpp", "k.hip"]
+    h0 = bench.kernel_source_hash("k.hip", str(src))
+    (src / "other.hip").write_text("int h2();\n")      # another unit: no effect
+    assert bench.kernel_source_hash("k.hip", str(src)) == h0
+    (src / "a.hpp").write_text("int g2();\n")          # an included header: stale
+    assert bench.kernel_source_hash("k.hip", str(src)) != h0
