@@ -30,9 +30,6 @@
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
-#ifndef FA_DKDV_WPE
-#define FA_DKDV_WPE 1
-#endif
 
 namespace fa {
 
@@ -42,7 +39,9 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) {
 }
 
 // D[h][r] = sum_d dO[r][h][d] O[r][h][d] and LSE[r][h] log2(e), one group of
-// D/8 lanes per (row, head).
+// D/8 lanes per (row, head).  Workspace rows past the last query row (up to
+// the padded stride) get D = 0 and LSE log2(e) = +inf, so a tile that reads
+// past its sequence sees P = 0 and finite D there.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const BwdParams p) {
   constexpr int LPP = D / 8;
@@ -66,10 +65,10 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const BwdParams p) 
   }
 #pragma unroll
   for (int m = LPP / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (valid && sub == 0) {
+  if (sub == 0 && r < p.ws_stride) {
     const size_t w = (size_t)h * p.ws_stride + r;
-    p.dsum[w] = acc;
-    p.lse2[w] = p.lse[(size_t)r * p.hq + h] * kLog2e;  // -inf stays -inf
+    p.dsum[w] = acc;  // 0 past the rows
+    p.lse2[w] = valid ? p.lse[(size_t)r * p.hq + h] * kLog2e : INFINITY;  // -inf stays -inf
   }
 }
 
@@ -99,6 +98,51 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float sc
                          pack_bf16x2(acc[dt][4 * g + 2] * scale, acc[dt][4 * g + 3] * scale)};
         *reinterpret_cast<u32x2*>(op + dt * 32 + 8 * g) = w;
       }
+  }
+}
+
+// Two independent 32 x 32 score products over the head dimension, their
+// MFMA chains interleaved: x = A_x B_x^T and y = A_y B_y^T with A_x, A_y rows
+// of swizzled LDS tiles and B_x, B_y fragments in registers.  The operands
+// of step st+1 are read while step st's MFMAs run.
+template <int D>
+__device__ __forceinline__ void scores_pair(f32x16& x, f32x16& y, const char* __restrict__ ax,
+                                            const char* __restrict__ ay, const LdsRead<D>& rd,
+                                            const bf16x8 (&bx)[D / 16],
+                                            const bf16x8 (&by)[D / 16]) {
+  bf16x8 a[2], b[2];
+  a[0] = rd.k(ax, 0, 0);
+  b[0] = rd.k(ay, 0, 0);
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    if (st + 1 < D / 16) {
+      a[(st + 1) & 1] = rd.k(ax, 0, st + 1);
+      b[(st + 1) & 1] = rd.k(ay, 0, st + 1);
+    }
+    x = mfma_32x32x16(a[st & 1], bx[st], st == 0 ? f32x16{} : x);
+    y = mfma_32x32x16(b[st & 1], by[st], st == 0 ? f32x16{} : y);
+  }
+}
+
+// dS^T = P^T * (dP^T - D) for NKT 32-key sub-tiles of one wave's rows (lanes),
+// rounded to bf16 in the order of the dQ product's B operand.  `lim` is the
+// last admissible key of the lane's row relative to the first sub-tile, minus
+// the lane's key offset; rows without data are zeroed.
+template <int NKT>
+__device__ __forceinline__ void dq_scores(const f32x16 (&s)[NKT][1], const f32x16 (&dp)[NKT][1],
+                                          bf16x8 (&dsb)[NKT][1][2], int lim, bool row_ok,
+                                          float lse2, float dsum, float c) {
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt) {
+    float ds[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const bool ok = row_ok && 32 * kt + (v & 3) + 8 * (v >> 2) <= lim;
+      const float pe = fast_exp2(fmaf(s[kt][0][v], c, -lse2));
+      ds[v] = ok ? pe * (dp[kt][0][v] - dsum) : 0.f;
+    }
+    dsb[kt][0][0] = pack_bf16x8(ds);
+    dsb[kt][0][1] = pack_bf16x8(ds + 8);
   }
 }
 
@@ -213,19 +257,9 @@ void bwd_dq_kernel(const BwdParams p) {
       const int ksub = j * BC + 32 * kt;
       if (ksub > wave_last_key) break;  // past this wave's keys (uniform)
       f32x16 s[1][1], dp[1][1];
-      scores_tile<D, 1, 1>(s, kc + kt * 64 * D, rd, st.qf);
-      scores_tile<D, 1, 1>(dp, vc + kt * 64 * D, rd, dof);
-      const int lim = row_lim - ksub;
-      float ds[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const bool ok = row_ok && (v & 3) + 8 * (v >> 2) <= lim;
-        const float pe = ok ? fast_exp2(fmaf(s[0][0][v], p.c, -lse2)) : 0.f;
-        ds[v] = ok ? pe * (dp[0][0][v] - dsum) : 0.f;
-      }
+      scores_pair<D>(s[0][0], dp[0][0], kc + kt * 64 * D, vc + kt * 64 * D, rd, st.qf[0], dof[0]);
       bf16x8 dsb[1][1][2];
-      dsb[0][0][0] = pack_bf16x8(ds);
-      dsb[0][0][1] = pack_bf16x8(ds + 8);
+      dq_scores<1>(s, dp, dsb, row_lim - ksub, row_ok, lse2, dsum, p.c);
       pv_tile<D, 1, 1>(st, kc + kt * 64 * D, rd, dsb);  // dQ^T += K^T dS^T
     }
   }
@@ -234,18 +268,25 @@ void bwd_dq_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: each wave owns 32 keys (one per lane column).  Per 32-query
-// sub-tile of the streamed Q / dO tiles it forms S = Q K^T and dP = dO V^T
-// (rows = queries), P and dS in registers with the query rows' LSE and D,
-// then dV^T += dO^T P and dK^T += Q^T dS.  The rows' LSE log2(e) and D ride
-// along with each Q / dO tile into LDS, so the inner loop reads no global
-// memory.
+// dK, dV: the workgroup owns BK = 128 keys in four 32-key columns, and each
+// column has two waves with split roles (the four "S" waves and the four
+// "dP" waves share the SIMDs in pairs).  Per 64-query tile of Q and dO, with
+// the rows' LSE log2(e) and D staged alongside in LDS:
+//   S wave (K row in registers):  S = Q K^T, P = exp2(S c - LSE log2 e) into
+//                                 LDS, dV^T += dO^T P
+//   dP wave (V row in registers): dP = dO V^T, then (after the exchange)
+//                                 dS = P (dP - D), dK^T += Q^T dS
+// Each wave holds one D x 32 accumulator, half of what a wave owning both
+// gradients needs, which lets two waves share a SIMD and hide each other's
+// elementwise work and LDS latency.  Two barriers per tile: the tile has
+// landed, and P has been written.
 // ---------------------------------------------------------------------------
-template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DKDV_WPE)))
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dkdv_kernel(const BwdParams p) {
+  constexpr int NW = 8;
   constexpr int BQ = 64;
-  constexpr int BK = NW * 32;
+  constexpr int BK = 128;
   constexpr int TILE = BQ * D * 2;
   constexpr int KS = D / 16;
   __shared__ __attribute__((aligned(1024))) char q_lds0[TILE];
@@ -255,11 +296,16 @@ void bwd_dkdv_kernel(const BwdParams p) {
   // per stage: LSE log2(e) of the tile's 64 rows, then their D (the DMA
   // instruction fills 1 KB; the second half repeats the first)
   __shared__ __attribute__((aligned(1024))) float st_lds[2][256];
+  // P of each column's two 32-row sub-tiles, fp32, in accumulator order:
+  // [column][sub-tile][register group][lane] of f32x4
+  __shared__ __attribute__((aligned(1024))) f32x4 p_lds[4][2][4][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int m32 = lane & 31, hh = lane >> 5;
+  const int col = wave & 3;
+  const bool dp_role = wave >= 4;  // uniform per wave
+  const int hh = lane >> 5, m32 = lane & 31;
 
   const int total = p.batch * p.hkv * p.n_kblocks;
   const int item = xcd_remap(blockIdx.x, total, p.n_kblocks);
@@ -286,31 +332,27 @@ void bwd_dkdv_kernel(const BwdParams p) {
   // rows at or past this bound have no workspace entry (a launch sized for
   // fewer rows than the sequences hold); they are masked like padding
   const int lq_eff = min(Lq, p.rows_cap - q_start);
-  const int kw0 = k0 + wave * 32;
+  const int kw0 = k0 + col * 32;
   const int key = kw0 + m32;
   const bool key_ok = key < Lk;
 
   const size_t q_stride = (size_t)p.hq * D;
   const size_t kv_stride = (size_t)p.hkv * D;
-  // this lane's key row of K and V (zeros past the end: their gradients are
-  // accumulated but never stored)
-  bf16x8 kf[1][KS], vf[1][KS];
+  // the lane's key row of K (S wave) or V (dP wave); zeros past the end
+  // (their gradients are accumulated but never stored)
+  bf16x8 frag[1][KS];
   {
+    const uint16_t* src = dp_role ? p.v : p.k;
     const size_t off = (size_t)(k_start + key) * kv_stride + (size_t)kvh * D + 8 * hh;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      u32x4 rk = {0u, 0u, 0u, 0u}, rv = {0u, 0u, 0u, 0u};
-      if (key_ok) {
-        rk = *reinterpret_cast<const u32x4*>(p.k + off + 16 * s);
-        rv = *reinterpret_cast<const u32x4*>(p.v + off + 16 * s);
-      }
-      kf[0][s] = __builtin_bit_cast(bf16x8, rk);
-      vf[0][s] = __builtin_bit_cast(bf16x8, rv);
+      u32x4 r = {0u, 0u, 0u, 0u};
+      if (key_ok) r = *reinterpret_cast<const u32x4*>(src + off + 16 * s);
+      frag[0][s] = __builtin_bit_cast(bf16x8, r);
     }
   }
-  WaveState<D, 1> sk, sv;  // o: dK^T and dV^T accumulators
-  sk.init();
-  sv.init();
+  WaveState<D, 1> acc;  // o: dV^T (S wave) or dK^T (dP wave)
+  acc.init();
 
   // Queries that see key j satisfy i >= j - delta (causal): start at the tile
   // holding the first query that sees this block's first key.
@@ -349,51 +391,75 @@ void bwd_dkdv_kernel(const BwdParams p) {
     const char* dc = stage ? do_lds1 : do_lds0;
     const float* stl = st_lds[stage];
     wait_dma();
-    __syncthreads();  // this tile has landed; everyone is done with the other stage
+    __syncthreads();  // this tile has landed; everyone is done with the other stage and P
     if (step + 1 < n_steps) issue(step + 1, stage ^ 1);
-    if (kw0 >= Lk) continue;  // this wave has no keys (uniform)
     const int q0 = (qt0 + step % per_head) * BQ;
+    // no key in this column, or every key above the diagonal: the column's
+    // two waves only keep the barriers
+    const bool active = kw0 < Lk && !(CAUSAL && kw0 > q0 + BQ - 1 + delta);
+    const int nsub = min(2, (Lq - q0 + 31) / 32);  // sub-tiles holding rows
+    f32x16 x[2][1];  // S (S wave) or dP (dP wave) per sub-tile
+    bf16x8 pk[2][1][2];
+    if (active) {
+      // both sub-tiles' chains interleaved (a missing second sub-tile reads
+      // clamped rows; its result is not used)
+      scores_tile<D, 1, 2>(x, dp_role ? dc : qc, rd, frag);
+      if (!dp_role) {
+        const bool full = q0 + BQ - 1 < lq_eff && (!CAUSAL || kw0 + 31 <= q0 + delta);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int qsub = q0 + 32 * kt;
-      if (qsub >= Lq) break;                            // past the queries (uniform)
-      if (CAUSAL && kw0 > qsub + 31 + delta) continue;  // every key above the diagonal
-      f32x16 s[1][1], dp[1][1];
-      scores_tile<D, 1, 1>(s, qc + kt * 64 * D, rd, kf);   // S = Q K^T
-      scores_tile<D, 1, 1>(dp, dc + kt * 64 * D, rd, vf);  // dP = dO V^T
-      // the lane's rows are qsub + 8 g + 4 hh + 0..3 for register group g
-      const bool full = qsub + 31 < lq_eff && (!CAUSAL || kw0 + 31 <= qsub + delta);
-      const int lo = key - delta - qsub - 4 * hh;  // first admissible row offset (causal)
-      const int hi = lq_eff - 1 - qsub - 4 * hh;   // last row offset with data
-      float pe[16], ds[16];
+        for (int kt = 0; kt < 2; ++kt) {
+          if (kt >= nsub) break;
+          const int qsub = q0 + 32 * kt;
+          const int lo = key - delta - qsub - 4 * hh;  // first admissible row offset (causal)
+          const int hi = lq_eff - 1 - qsub - 4 * hh;   // last row offset with data
+          float pe[16];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(stl + 32 * kt + 8 * g + 4 * hh);
-        const f32x4 dd = *reinterpret_cast<const f32x4*>(stl + 64 + 32 * kt + 8 * g + 4 * hh);
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 l2 = *reinterpret_cast<const f32x4*>(stl + 32 * kt + 8 * g + 4 * hh);
+            f32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int v = 4 * g + e;
-          const float pv = fast_exp2(fmaf(s[0][0][v], p.c, -l2[e]));
-          const float dv = pv * (dp[0][0][v] - dd[e]);
-          const int r = 8 * g + e;
-          const bool ok = full || (r <= hi && (!CAUSAL || r >= lo));
-          pe[v] = ok ? pv : 0.f;
-          ds[v] = ok ? dv : 0.f;
+            for (int e = 0; e < 4; ++e) {
+              const int r = 8 * g + e;
+              const bool ok = full || (r <= hi && (!CAUSAL || r >= lo));
+              const float pv = fast_exp2(fmaf(x[kt][0][4 * g + e], p.c, -l2[e]));
+              pe[4 * g + e] = ok ? pv : 0.f;
+              w[e] = pe[4 * g + e];
+            }
+            p_lds[col][kt][g][lane] = w;
+          }
+          pk[kt][0][0] = pack_bf16x8(pe);
+          pk[kt][0][1] = pack_bf16x8(pe + 8);
         }
       }
-      bf16x8 pb[1][1][2], dsb[1][1][2];
-      pb[0][0][0] = pack_bf16x8(pe);
-      pb[0][0][1] = pack_bf16x8(pe + 8);
-      dsb[0][0][0] = pack_bf16x8(ds);
-      dsb[0][0][1] = pack_bf16x8(ds + 8);
-      pv_tile<D, 1, 1>(sv, dc + kt * 64 * D, rd, pb);   // dV^T += dO^T P
-      pv_tile<D, 1, 1>(sk, qc + kt * 64 * D, rd, dsb);  // dK^T += Q^T dS
+    }
+    __syncthreads();  // P of this tile is in LDS
+    if (active) {
+      if (dp_role) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          if (kt >= nsub) break;
+          float ds[16];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 dd = *reinterpret_cast<const f32x4*>(stl + 64 + 32 * kt + 8 * g + 4 * hh);
+            const f32x4 pv = p_lds[col][kt][g][lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              ds[4 * g + e] = pv[e] * (x[kt][0][4 * g + e] - dd[e]);
+          }
+          pk[kt][0][0] = pack_bf16x8(ds);
+          pk[kt][0][1] = pack_bf16x8(ds + 8);
+        }
+      }
+      // dV^T += dO^T P (S wave) or dK^T += Q^T dS (dP wave)
+      if (nsub < 2) pk[1][0][0] = pk[1][0][1] = bf16x8{};  // no rows: contributes nothing
+      pv_tile<D, 1, 2>(acc, dp_role ? qc : dc, rd, pk);
     }
   }
   if (key_ok) {
     const size_t off = ((size_t)(k_start + key) * p.hkv + kvh) * D;
-    store_rows<D>(sk.o[0], p.scale, p.dk, off, p.g_f32, hh);
-    store_rows<D>(sv.o[0], 1.f, p.dv, off, p.g_f32, hh);
+    if (dp_role) store_rows<D>(acc.o[0], p.scale, p.dk, off, p.g_f32, hh);
+    else store_rows<D>(acc.o[0], 1.f, p.dv, off, p.g_f32, hh);
   }
 }
 
@@ -403,18 +469,18 @@ template __global__ void bwd_dq_kernel<128, 4, false>(const BwdParams);
 template __global__ void bwd_dq_kernel<128, 4, true>(const BwdParams);
 template __global__ void bwd_dq_kernel<64, 4, false>(const BwdParams);
 template __global__ void bwd_dq_kernel<64, 4, true>(const BwdParams);
-template __global__ void bwd_dkdv_kernel<128, 4, false>(const BwdParams);
-template __global__ void bwd_dkdv_kernel<128, 4, true>(const BwdParams);
-template __global__ void bwd_dkdv_kernel<64, 4, false>(const BwdParams);
-template __global__ void bwd_dkdv_kernel<64, 4, true>(const BwdParams);
+template __global__ void bwd_dkdv_kernel<128, false>(const BwdParams);
+template __global__ void bwd_dkdv_kernel<128, true>(const BwdParams);
+template __global__ void bwd_dkdv_kernel<64, false>(const BwdParams);
+template __global__ void bwd_dkdv_kernel<64, true>(const BwdParams);
 
 constexpr int kBwdWaves = 4;
 int bwd_dq_rows() { return kBwdWaves * 32; }
-int bwd_dkdv_keys() { return kBwdWaves * 32; }
+int bwd_dkdv_keys() { return 128; }
 
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
-  const long long pairs = (long long)p.rows_cap * p.hq;
+  const long long pairs = (long long)p.ws_stride * p.hq;
   const int ppb = 256 / (D / 8);
   const int n_kv = p.batch * p.hkv * p.n_kblocks, n_q = p.batch * p.hq * p.n_qtiles;
   // A side with no rows launches nothing: with no queries the dK/dV kernel
@@ -423,8 +489,7 @@ static hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_preprocess_kernel<D>, dim3((unsigned)((pairs + ppb - 1) / ppb)),
                        dim3(256), 0, stream, p);
   if (n_kv > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kBwdWaves, CAUSAL>), dim3(n_kv),
-                       dim3(kBwdWaves * 64), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_kv), dim3(512), 0, stream, p);
   if (n_q > 0)
     hipLaunchKernelGGL((bwd_dq_kernel<D, kBwdWaves, CAUSAL>), dim3(n_q), dim3(kBwdWaves * 64),
                        0, stream, p);
