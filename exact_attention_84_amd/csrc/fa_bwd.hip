@@ -27,6 +27,8 @@
 // pv_tile (A = an LDS tile read transposed, B = bf16 probabilities in the
 // accumulator order) gives dQ^T += K^T dS^T, dV^T += dO^T P and
 // dK^T += Q^T dS.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -101,26 +103,127 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float sc
   }
 }
 
+// LDS byte address of a pointer into a __shared__ array, held in a VGPR the
+// compiler cannot see through: operand addresses are then formed as this
+// register plus the lane's offset, with the sub-tile offset folded into the
+// instruction's immediate (one add per read instead of two).
+typedef __attribute__((address_space(3))) const char lds_cchar;
+__device__ __forceinline__ uint32_t lds_base(const char* p) {
+  uint32_t a = (uint32_t)(uintptr_t)(lds_cchar*)p;
+  asm volatile("" : "+v"(a));
+  return a;
+}
+template <typename T>
+__device__ __forceinline__ T lds_load(uint32_t a) {
+  return *(const __attribute__((address_space(3))) T*)(uintptr_t)a;
+}
+typedef short s16x4b __attribute__((ext_vector_type(4)));
+typedef short s16x8b __attribute__((ext_vector_type(8)));
+
+// Per-lane operand base addresses of one swizzled tile, each an opaque VGPR,
+// so that every read is a single LDS instruction with the sub-tile / row-step
+// offset in its immediate.
+template <int D>
+struct KBases {  // score operand (rows kt*32 + lane%32, head-dim step st)
+  uint32_t b[D / 16];
+  __device__ __forceinline__ KBases(uint32_t t, const LdsRead<D>& rd) {
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      b[st] = t + rd.kb[st];
+      asm volatile("" : "+v"(b[st]));
+    }
+  }
+  __device__ __forceinline__ bf16x8 read(int kt, int st) const {
+    return lds_load<bf16x8>(b[st] + kt * 64 * D);
+  }
+};
+template <int D>
+struct VBases {  // transposed operand (head-dim block dt, 16-row step (kt, u))
+  uint32_t b[D / 32][2];
+  __device__ __forceinline__ VBases(uint32_t t, const LdsRead<D>& rd) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int sec = 0; sec < 2; ++sec) {
+        b[dt][sec] = t + rd.vb[dt][sec];
+        asm volatile("" : "+v"(b[dt][sec]));
+      }
+  }
+  __device__ __forceinline__ bf16x8 read(int kt, int u, int dt) const {
+    const uint32_t row = (kt * 32 + 16 * u) * 2 * D;
+    const s16x4b lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4b*)(uintptr_t)(b[dt][0] + row));
+    const s16x4b hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4b*)(uintptr_t)(b[dt][1] + row));
+    const s16x8b w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, w);
+  }
+};
+
+// The backward's MFMA sequences, with their LDS operands read two MFMAs
+// ahead (LDS latency is longer than one 32-cycle MFMA).
+//
+// scores_pf: X_kt = A_kt B^T for the NKT 32-row sub-tiles of a swizzled LDS
+// tile (A) and a fragment in registers (B), the sub-tiles' chains
+// interleaved.
+template <int D, int NKT>
+__device__ __forceinline__ void scores_pf(f32x16 (&x)[NKT][1], const char* __restrict__ lds,
+                                          const LdsRead<D>& rd, const bf16x8 (&b)[1][D / 16]) {
+  constexpr int N = NKT * (D / 16);
+  const KBases<D> kb(lds_base(lds), rd);
+  bf16x8 op[3];
+  auto read = [&](int i) { return kb.read(i % NKT, i / NKT); };
+  op[0] = read(0);
+  op[1] = read(1);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + 2 < N) op[(i + 2) % 3] = read(i + 2);
+    const int kt = i % NKT, st = i / NKT;
+    x[kt][0] = mfma_32x32x16(op[i % 3], b[0][st], st == 0 ? f32x16{} : x[kt][0]);
+  }
+}
+
+// pv_pf: acc^T += A_kt^T P_kt over NKT 32-row sub-tiles of a swizzled LDS
+// tile read transposed (A) and bf16 operands in accumulator order (P).
+template <int D, int NKT>
+__device__ __forceinline__ void pv_pf(f32x16 (&acc)[D / 32], const char* __restrict__ lds,
+                                      const LdsRead<D>& rd, const bf16x8 (&pb)[NKT][1][2]) {
+  constexpr int DT = D / 32;
+  constexpr int N = NKT * 2 * DT;
+  const VBases<D> vb(lds_base(lds), rd);
+  bf16x8 op[3];
+  auto read = [&](int i) { return vb.read(i / (2 * DT), (i / DT) & 1, i % DT); };
+  op[0] = read(0);
+  op[1] = read(1);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + 2 < N) op[(i + 2) % 3] = read(i + 2);
+    const int kt = i / (2 * DT), u = (i / DT) & 1, dt = i % DT;
+    acc[dt] = mfma_32x32x16(op[i % 3], pb[kt][0][u], acc[dt]);
+  }
+}
+
 // Two independent 32 x 32 score products over the head dimension, their
 // MFMA chains interleaved: x = A_x B_x^T and y = A_y B_y^T with A_x, A_y rows
-// of swizzled LDS tiles and B_x, B_y fragments in registers.  The operands
-// of step st+1 are read while step st's MFMAs run.
+// of swizzled LDS tiles and B_x, B_y fragments in registers.  Operands are
+// read two MFMAs ahead.
 template <int D>
 __device__ __forceinline__ void scores_pair(f32x16& x, f32x16& y, const char* __restrict__ ax,
                                             const char* __restrict__ ay, const LdsRead<D>& rd,
                                             const bf16x8 (&bx)[D / 16],
                                             const bf16x8 (&by)[D / 16]) {
-  bf16x8 a[2], b[2];
-  a[0] = rd.k(ax, 0, 0);
-  b[0] = rd.k(ay, 0, 0);
+  constexpr int N = 2 * (D / 16);  // MFMAs, alternating x and y
+  const KBases<D> kx(lds_base(ax), rd), ky(lds_base(ay), rd);
+  bf16x8 op[3];
+  auto read = [&](int i) { return (i & 1) ? ky.read(0, i >> 1) : kx.read(0, i >> 1); };
+  op[0] = read(0);
+  op[1] = read(1);
 #pragma unroll
-  for (int st = 0; st < D / 16; ++st) {
-    if (st + 1 < D / 16) {
-      a[(st + 1) & 1] = rd.k(ax, 0, st + 1);
-      b[(st + 1) & 1] = rd.k(ay, 0, st + 1);
-    }
-    x = mfma_32x32x16(a[st & 1], bx[st], st == 0 ? f32x16{} : x);
-    y = mfma_32x32x16(b[st & 1], by[st], st == 0 ? f32x16{} : y);
+  for (int i = 0; i < N; ++i) {
+    if (i + 2 < N) op[(i + 2) % 3] = read(i + 2);
+    const int st = i >> 1;
+    if (i & 1) y = mfma_32x32x16(op[i % 3], by[st], st == 0 ? f32x16{} : y);
+    else x = mfma_32x32x16(op[i % 3], bx[st], st == 0 ? f32x16{} : x);
   }
 }
 
@@ -260,7 +363,7 @@ void bwd_dq_kernel(const BwdParams p) {
       scores_pair<D>(s[0][0], dp[0][0], kc + kt * 64 * D, vc + kt * 64 * D, rd, st.qf[0], dof[0]);
       bf16x8 dsb[1][1][2];
       dq_scores<1>(s, dp, dsb, row_lim - ksub, row_ok, lse2, dsum, p.c);
-      pv_tile<D, 1, 1>(st, kc + kt * 64 * D, rd, dsb);  // dQ^T += K^T dS^T
+      pv_pf<D, 1>(st.o[0], kc + kt * 64 * D, rd, dsb);  // dQ^T += K^T dS^T
     }
   }
   if (row_ok)
@@ -279,7 +382,10 @@ void bwd_dq_kernel(const BwdParams p) {
 // Each wave holds one D x 32 accumulator, half of what a wave owning both
 // gradients needs, which lets two waves share a SIMD and hide each other's
 // elementwise work and LDS latency.  Two barriers per tile: the tile has
-// landed, and P has been written.
+// landed, and P has been written.  The dP wave applies each tile's dK product
+// one tile late, while its partner computes the next tile's exponentials, so
+// the SIMD's matrix unit has work during them; Q tiles are therefore
+// triple-buffered.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
@@ -289,10 +395,8 @@ void bwd_dkdv_kernel(const BwdParams p) {
   constexpr int BK = 128;
   constexpr int TILE = BQ * D * 2;
   constexpr int KS = D / 16;
-  __shared__ __attribute__((aligned(1024))) char q_lds0[TILE];
-  __shared__ __attribute__((aligned(1024))) char q_lds1[TILE];
-  __shared__ __attribute__((aligned(1024))) char do_lds0[TILE];
-  __shared__ __attribute__((aligned(1024))) char do_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) char q_lds[3][TILE];
+  __shared__ __attribute__((aligned(1024))) char do_lds[2][TILE];
   // per stage: LSE log2(e) of the tile's 64 rows, then their D (the DMA
   // instruction fills 1 KB; the second half repeats the first)
   __shared__ __attribute__((aligned(1024))) float st_lds[2][256];
@@ -365,14 +469,15 @@ void bwd_dkdv_kernel(const BwdParams p) {
   dma.init(q_stride, wave, lane);
   LdsRead<D> rd;
   rd.init(lane);
-  auto issue = [&](int step, int stage) {
+  auto issue = [&](int step) {
+    const int stage = step & 1;
     const int hg = step / per_head, q0 = (qt0 + step % per_head) * BQ;
     const int h = p.group * kvh + hg;
     const size_t head = (size_t)h * D;
     const uint16_t* qb = p.q + (size_t)q_start * q_stride + head;
     const uint16_t* db = p.dout + (size_t)q_start * q_stride + head;
-    dma.issue(qb, q_stride, q0, Lq - 1, stage ? q_lds1 : q_lds0, wave, lane);
-    dma.issue(db, q_stride, q0, Lq - 1, stage ? do_lds1 : do_lds0, wave, lane);
+    dma.issue(qb, q_stride, q0, Lq - 1, q_lds[step % 3], wave, lane);
+    dma.issue(db, q_stride, q0, Lq - 1, do_lds[stage], wave, lane);
     if (wave == 0) {
       // 16 lanes x 16 bytes per statistic; the row base is clamped so the
       // 64-row read stays inside the workspace (its 64 rows of padding)
@@ -382,80 +487,116 @@ void bwd_dkdv_kernel(const BwdParams p) {
       __builtin_amdgcn_global_load_lds(src, (lds_void*)st_lds[stage], 16, 0, 0);
     }
   };
-  if (n_steps > 0) issue(0, 0);
+  if (n_steps > 0) issue(0);
 
-#pragma clang loop unroll(disable)
-  for (int step = 0; step < n_steps; ++step) {
-    const int stage = step & 1;
-    const char* qc = stage ? q_lds1 : q_lds0;
-    const char* dc = stage ? do_lds1 : do_lds0;
-    const float* stl = st_lds[stage];
-    wait_dma();
-    __syncthreads();  // this tile has landed; everyone is done with the other stage and P
-    if (step + 1 < n_steps) issue(step + 1, stage ^ 1);
-    const int q0 = (qt0 + step % per_head) * BQ;
-    // no key in this column, or every key above the diagonal: the column's
-    // two waves only keep the barriers
-    const bool active = kw0 < Lk && !(CAUSAL && kw0 > q0 + BQ - 1 + delta);
-    const int nsub = min(2, (Lq - q0 + 31) / 32);  // sub-tiles holding rows
-    f32x16 x[2][1];  // S (S wave) or dP (dP wave) per sub-tile
+  // The step loop, instantiated once per role so that each role's registers
+  // are allocated for its own live values.  Both loops meet the same two
+  // barriers per tile.
+  auto run = [&](auto role) {
+    constexpr bool DPR = decltype(role)::value;
+    // bf16 B operands of the accumulator's product: the S wave's P (formed
+    // and used within a tile) or the dP wave's dS (formed in one tile, used
+    // in the next)
     bf16x8 pk[2][1][2];
-    if (active) {
-      // both sub-tiles' chains interleaved (a missing second sub-tile reads
-      // clamped rows; its result is not used)
-      scores_tile<D, 1, 2>(x, dp_role ? dc : qc, rd, frag);
-      if (!dp_role) {
-        const bool full = q0 + BQ - 1 < lq_eff && (!CAUSAL || kw0 + 31 <= q0 + delta);
+    bool have_prev = false;
+#pragma clang loop unroll(disable)
+    for (int step = 0; step < n_steps; ++step) {
+      const int stage = step & 1;
+      const char* qc = q_lds[step % 3];
+      const char* dc = do_lds[stage];
+      const float* stl = st_lds[stage];
+      wait_dma();
+      __syncthreads();  // this tile has landed; everyone is done with the other stages and P
+      const int q0 = (qt0 + step % per_head) * BQ;
+      // no key in this column, or every key above the diagonal: the column's
+      // two waves only keep the barriers
+      const bool active = kw0 < Lk && !(CAUSAL && kw0 > q0 + BQ - 1 + delta);
+      const int nsub = min(2, (Lq - q0 + 31) / 32);  // sub-tiles holding rows
+      f32x16 x[2][1];  // S (S wave) or dP (dP wave) per sub-tile
+      // The next tile's loads are issued while this wave's first products
+      // run (issuing them right at the barrier queues all eight waves' loads
+      // at once).  The dP wave first applies the previous tile's dK product
+      // (its Q tile is still resident: three Q stages), then forms dP; the S
+      // wave forms S.  Both score products interleave their two sub-tiles'
+      // chains (a missing second sub-tile reads clamped rows; its result is
+      // not used).
+      if constexpr (DPR) {
+        if (have_prev) pv_pf<D, 2>(acc.o[0], q_lds[(step + 2) % 3], rd, pk);
+        if (step + 1 < n_steps) issue(step + 1);
+        if (active) scores_pf<D, 2>(x, dc, rd, frag);
+      } else {
+        if (active) scores_pf<D, 2>(x, qc, rd, frag);
+        if (step + 1 < n_steps) issue(step + 1);
+      }
+      if constexpr (!DPR) {
+        if (active) {
+          const bool full = q0 + BQ - 1 < lq_eff && (!CAUSAL || kw0 + 31 <= q0 + delta);
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          if (kt >= nsub) break;
-          const int qsub = q0 + 32 * kt;
-          const int lo = key - delta - qsub - 4 * hh;  // first admissible row offset (causal)
-          const int hi = lq_eff - 1 - qsub - 4 * hh;   // last row offset with data
-          float pe[16];
+          for (int kt = 0; kt < 2; ++kt) {
+            if (kt >= nsub) break;
+            const int qsub = q0 + 32 * kt;
+            const int lo = key - delta - qsub - 4 * hh;  // first admissible row offset (causal)
+            const int hi = lq_eff - 1 - qsub - 4 * hh;   // last row offset with data
+            float pe[16];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 l2 = *reinterpret_cast<const f32x4*>(stl + 32 * kt + 8 * g + 4 * hh);
-            f32x4 w;
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 l2 = *reinterpret_cast<const f32x4*>(stl + 32 * kt + 8 * g + 4 * hh);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 8 * g + e;
-              const bool ok = full || (r <= hi && (!CAUSAL || r >= lo));
-              const float pv = fast_exp2(fmaf(x[kt][0][4 * g + e], p.c, -l2[e]));
-              pe[4 * g + e] = ok ? pv : 0.f;
-              w[e] = pe[4 * g + e];
+              for (int e = 0; e < 4; ++e)
+                pe[4 * g + e] = fast_exp2(fmaf(x[kt][0][4 * g + e], p.c, -l2[e]));
             }
-            p_lds[col][kt][g][lane] = w;
+            if (!full) {  // edge tile (uniform per wave)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                const int r = (v & 3) + 8 * (v >> 2);
+                pe[v] = (r <= hi && (!CAUSAL || r >= lo)) ? pe[v] : 0.f;
+              }
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              p_lds[col][kt][g][lane] =
+                  f32x4{pe[4 * g], pe[4 * g + 1], pe[4 * g + 2], pe[4 * g + 3]};
+            pk[kt][0][0] = pack_bf16x8(pe);
+            pk[kt][0][1] = pack_bf16x8(pe + 8);
           }
-          pk[kt][0][0] = pack_bf16x8(pe);
-          pk[kt][0][1] = pack_bf16x8(pe + 8);
+        }
+      }
+      __syncthreads();  // P of this tile is in LDS
+      if constexpr (DPR) {
+        have_prev = active;
+        if (active) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            if (kt >= nsub) break;
+            float ds[16];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 dd =
+                  *reinterpret_cast<const f32x4*>(stl + 64 + 32 * kt + 8 * g + 4 * hh);
+              const f32x4 pv = p_lds[col][kt][g][lane];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) ds[4 * g + e] = pv[e] * (x[kt][0][4 * g + e] - dd[e]);
+            }
+            pk[kt][0][0] = pack_bf16x8(ds);
+            pk[kt][0][1] = pack_bf16x8(ds + 8);
+          }
+          if (nsub < 2) pk[1][0][0] = pk[1][0][1] = bf16x8{};  // no rows
+        }
+      } else {
+        if (active) {
+          if (nsub < 2) pk[1][0][0] = pk[1][0][1] = bf16x8{};  // no rows: contributes nothing
+          pv_pf<D, 2>(acc.o[0], dc, rd, pk);  // dV^T += dO^T P
         }
       }
     }
-    __syncthreads();  // P of this tile is in LDS
-    if (active) {
-      if (dp_role) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          if (kt >= nsub) break;
-          float ds[16];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 dd = *reinterpret_cast<const f32x4*>(stl + 64 + 32 * kt + 8 * g + 4 * hh);
-            const f32x4 pv = p_lds[col][kt][g][lane];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              ds[4 * g + e] = pv[e] * (x[kt][0][4 * g + e] - dd[e]);
-          }
-          pk[kt][0][0] = pack_bf16x8(ds);
-          pk[kt][0][1] = pack_bf16x8(ds + 8);
-        }
-      }
-      // dV^T += dO^T P (S wave) or dK^T += Q^T dS (dP wave)
-      if (nsub < 2) pk[1][0][0] = pk[1][0][1] = bf16x8{};  // no rows: contributes nothing
-      pv_tile<D, 1, 2>(acc, dp_role ? qc : dc, rd, pk);
+    // the last tile's dK product (its Q tile stays resident)
+    if constexpr (DPR) {
+      if (have_prev) pv_pf<D, 2>(acc.o[0], q_lds[(n_steps - 1) % 3], rd, pk);
     }
-  }
+  };
+  if (dp_role) run(std::true_type{});
+  else run(std::false_type{});
+
   if (key_ok) {
     const size_t off = ((size_t)(k_start + key) * p.hkv + kvh) * D;
     if (dp_role) store_rows<D>(acc.o[0], p.scale, p.dk, off, p.g_f32, hh);
