@@ -88,7 +88,7 @@ TRAFFIC_KERNELS = {
     "fwd_kernel<128, 8, 1, false, false>": ("fwd_noncausal_d128", "fa_fwd.hip"),
     "fwd_kernel<128, 8, 1, true, true>": ("fwd_causal_d128", "fa_fwd.hip"),
     "decode_kernel<128>": ("decode_d128", "fa_decode.hip"),
-    "bwd_dkdv_kernel<128, 4, false>": ("bwd_dkdv_noncausal_d128", "fa_bwd.hip"),
+    "bwd_dkdv_kernel<128, false>": ("bwd_dkdv_noncausal_d128", "fa_bwd.hip"),
     "bwd_dq_kernel<128, 4, false>": ("bwd_dq_noncausal_d128", "fa_bwd.hip"),
 }
 
