@@ -27,3 +27,11 @@ from .grad import (  # noqa: F401
     probabilities,
     softmax_backward,
 )
+from .kvcache import (  # noqa: F401
+    bf16_bits,
+    cache_row_index,
+    gather_rows,
+    kvcache_step,
+    rotary,
+    to_bf16_rne,
+)
