@@ -220,6 +220,89 @@ def decode(q, k_cache, v_cache, cache_seqlens, *, scale: float | None = None, ch
     return out, lse
 
 
+def decode_kvcache_workspace_size(batch: int, heads_q: int, max_cache_len: int, head_dim: int,
+                                  chunk: int = 0) -> int:
+    return int(load().fa_decode_kvcache_workspace_size(batch, heads_q, max_cache_len, head_dim,
+                                                       chunk))
+
+
+def decode_kvcache(q, k_cache, v_cache, cache_seqlens, *, k_new=None, v_new=None,
+                   block_table=None, rotary_cos=None, rotary_sin=None,
+                   rotary_interleaved: bool = False, scale: float | None = None, chunk: int = 0,
+                   out=None, lse=None, workspace=None, out_dtype=torch.bfloat16, stream=None):
+    """One decode step that updates the cache in place (``fa_fwd_decode_kvcache``).
+
+    q [B, Hq, d]; k_new/v_new [B, Hkv, d] or None; cache_seqlens int32 [B]
+    (tokens cached before the call; not modified).  Contiguous caches are
+    [B, Ncache, Hkv, d]; with ``block_table`` (int32 [B, max_blocks]) they are
+    paged [num_blocks, page_size, Hkv, d].  ``rotary_cos``/``rotary_sin`` are
+    fp32 [max_pos, rotary_dim / 2].  Returns (o [B, Hq, d], lse [B, Hq]).
+    """
+    lib = load()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    if out_dtype not in _OUT_DTYPES:
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    batch, hq, d = q.shape
+    if k_cache.shape != v_cache.shape or k_cache.shape[3] != d:
+        raise ValueError("cache shapes do not match q")
+    if cache_seqlens.numel() != batch:
+        raise ValueError("cache_seqlens must have one entry per sequence")
+    hkv = k_cache.shape[2]
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if k_new is not None:
+        for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+            _need(t, n, torch.bfloat16, 3)
+            if tuple(t.shape) != (batch, hkv, d):
+                raise ValueError(f"{n} must be [batch, heads_kv, head_dim]")
+    if block_table is not None:
+        _need(block_table, "block_table", torch.int32, 2)
+        if block_table.shape[0] != batch:
+            raise ValueError("block_table must have one row per sequence")
+        num_blocks, page = k_cache.shape[0], k_cache.shape[1]
+        max_blocks = block_table.shape[1]
+        cap = max_blocks * page
+    else:
+        if k_cache.shape[0] != batch:
+            raise ValueError("contiguous caches have one slice per sequence")
+        num_blocks = page = max_blocks = 0
+        cap = k_cache.shape[1]
+    if (rotary_cos is None) != (rotary_sin is None):
+        raise ValueError("rotary_cos and rotary_sin go together")
+    rdim = max_pos = 0
+    if rotary_cos is not None:
+        _need(rotary_cos, "rotary_cos", torch.float32, 2)
+        _need(rotary_sin, "rotary_sin", torch.float32, 2)
+        if rotary_cos.shape != rotary_sin.shape:
+            raise ValueError("rotary tables differ in shape")
+        max_pos, rdim = rotary_cos.shape[0], 2 * rotary_cos.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = lib.fa_decode_kvcache_workspace_size(batch, hq, cap, d, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _need(workspace, "workspace", torch.uint8)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    else:
+        _need(out, "out", out_dtype, 3)
+    if lse is None:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
+    else:
+        _need(lse, "lse", torch.float32, 2)
+    st = lib.fa_fwd_decode_kvcache(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(cache_seqlens),
+        _ptr(block_table), max_blocks, page, num_blocks, _ptr(rotary_cos), _ptr(rotary_sin), rdim,
+        max_pos, int(bool(rotary_interleaved)), _ptr(out), _ptr(lse), batch, hq, hkv, cap, d,
+        scale, int(chunk), _ptr(workspace), workspace.numel(), _OUT_DTYPES[out_dtype],
+        _stream_handle(stream))
+    check(st, "fa_fwd_decode_kvcache")
+    return out, lse
+
+
 def combine(o_part, lse_part, *, out=None, lse=None, out_dtype=torch.float32, stream=None):
     """LSE-weighted merge: o_part [rows, S, d] fp32, lse_part [rows, S] fp32
     (-inf = empty split) -> o [rows, d], lse [rows]."""

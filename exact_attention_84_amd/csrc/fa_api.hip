@@ -193,8 +193,42 @@ fa_status fa_fwd_decode_splitkv(const void* q, const void* k_cache, const void* 
                                 int heads_q, int heads_kv, int max_cache_len, int head_dim,
                                 float scale, int chunk, void* workspace, size_t workspace_bytes,
                                 fa_dtype o_dtype, void* stream) {
+  return fa_fwd_decode_kvcache(q, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+                               nullptr, nullptr, cache_seqlens, nullptr, 0, 0, 0, nullptr,
+                               nullptr, 0, 0, 0, o, lse, batch, heads_q, heads_kv, max_cache_len,
+                               head_dim, scale, chunk, workspace, workspace_bytes, o_dtype,
+                               stream);
+}
+
+// Bytes of the rotated-query buffer at the start of a KV-cache decode
+// workspace (256-byte aligned), when rotary is used.
+static size_t qrot_bytes(int batch, int heads_q, int head_dim) {
+  const size_t b = (size_t)batch * heads_q * head_dim * 2;
+  return (b + 255) / 256 * 256;
+}
+
+size_t fa_decode_kvcache_workspace_size(int batch, int heads_q, int max_cache_len, int head_dim,
+                                        int chunk) {
+  const size_t part = fa_decode_workspace_size(batch, heads_q, max_cache_len, head_dim, chunk);
+  if (part == 0) return 0;  // invalid sizes, or nothing to compute
+  return qrot_bytes(batch, heads_q, head_dim) + part;
+}
+
+fa_status fa_fwd_decode_kvcache(const void* q, void* k_cache, void* v_cache, const void* k_new,
+                                const void* v_new, const int32_t* cache_seqlens,
+                                const int32_t* block_table, int max_blocks_per_seq,
+                                int page_size, int num_blocks, const float* rotary_cos,
+                                const float* rotary_sin, int rotary_dim, int rotary_max_pos,
+                                int rotary_interleaved, void* o, float* lse, int batch,
+                                int heads_q, int heads_kv, int max_cache_len, int head_dim,
+                                float scale, int chunk, void* workspace, size_t workspace_bytes,
+                                fa_dtype o_dtype, void* stream) {
   if (!q || !k_cache || !v_cache || !cache_seqlens || !o || !lse)
     return fail(FA_ERR_NULL, "q, caches, cache_seqlens, o and lse must be non-NULL");
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(FA_ERR_NULL, "k_new and v_new must both be given or both be NULL");
+  if ((rotary_cos == nullptr) != (rotary_sin == nullptr))
+    return fail(FA_ERR_NULL, "rotary_cos and rotary_sin must both be given or both be NULL");
   if (!valid_head_dim(head_dim))
     return fail(FA_ERR_HEADDIM, "head_dim %d not supported (64 or 128)", head_dim);
   if (batch < 0 || heads_q <= 0 || heads_kv <= 0 || max_cache_len < 0)
@@ -210,11 +244,31 @@ fa_status fa_fwd_decode_splitkv(const void* q, const void* k_cache, const void* 
                 fa::kDecodeTile);
   if (o_dtype != FA_DTYPE_BF16 && o_dtype != FA_DTYPE_F32)
     return fail(FA_ERR_DTYPE, "o_dtype %d unknown", (int)o_dtype);
-  if ((long long)batch * max_cache_len * heads_kv * head_dim > kMaxElems)
+  const bool paged = block_table != nullptr;
+  if (paged) {
+    if (page_size <= 0 || page_size % fa::kDecodeTile)
+      return fail(FA_ERR_ARG, "page_size %d must be a positive multiple of %d", page_size,
+                  fa::kDecodeTile);
+    if (max_blocks_per_seq <= 0 || num_blocks <= 0)
+      return fail(FA_ERR_SHAPE, "max_blocks_per_seq and num_blocks must be > 0");
+    if ((long long)max_blocks_per_seq * page_size != max_cache_len)
+      return fail(FA_ERR_SHAPE, "paged: max_cache_len %d must equal max_blocks_per_seq * "
+                  "page_size = %lld", max_cache_len, (long long)max_blocks_per_seq * page_size);
+    if ((long long)num_blocks * page_size * heads_kv * head_dim > kMaxElems)
+      return fail(FA_ERR_SHAPE, "block pool too large");
+  } else if ((long long)batch * max_cache_len * heads_kv * head_dim > kMaxElems) {
     return fail(FA_ERR_SHAPE, "cache too large");
+  }
+  const bool rot = rotary_cos != nullptr;
+  if (rot && (rotary_dim <= 0 || rotary_dim % 2 || rotary_dim > head_dim || rotary_max_pos <= 0))
+    return fail(FA_ERR_ARG, "rotary_dim %d must be even, in (0, head_dim], with max_pos > 0",
+                rotary_dim);
+  if (rotary_interleaved != 0 && rotary_interleaved != 1)
+    return fail(FA_ERR_ARG, "rotary_interleaved must be 0 or 1");
   const int c = chunk ? chunk : default_decode_chunk(batch, heads_kv, max_cache_len);
   const int n_splits = decode_splits(max_cache_len, c);
-  const size_t need = fa_decode_workspace_size(batch, heads_q, max_cache_len, head_dim, c);
+  const size_t qrb = rot ? qrot_bytes(batch, heads_q, head_dim) : 0;
+  const size_t need = qrb + fa_decode_workspace_size(batch, heads_q, max_cache_len, head_dim, c);
   if (!workspace || workspace_bytes < need)
     return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -226,14 +280,42 @@ fa_status fa_fwd_decode_splitkv(const void* q, const void* k_cache, const void* 
 
   fa_status s = check_device();
   if (s != FA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+
+  if (rot || k_new) {
+    fa::AppendParams a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.q_rot = rot ? reinterpret_cast<uint16_t*>(ws) : nullptr;
+    a.k_cache = static_cast<uint16_t*>(k_cache);
+    a.v_cache = static_cast<uint16_t*>(v_cache);
+    a.cache_seqlens = cache_seqlens;
+    a.block_table = block_table;
+    a.max_blocks = max_blocks_per_seq;
+    a.page_size = page_size;
+    a.num_blocks = num_blocks;
+    a.cos = rotary_cos;
+    a.sin = rotary_sin;
+    a.rdim = rot ? rotary_dim : 0;
+    a.max_pos = rotary_max_pos;
+    a.interleaved = rotary_interleaved;
+    a.batch = batch;
+    a.hq = heads_q;
+    a.hkv = heads_kv;
+    a.cache_len = max_cache_len;
+    hipError_t e = fa::launch_append(a, head_dim, st);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "append launch: %s", hipGetErrorString(e));
+  }
 
   const size_t rows = (size_t)batch * heads_q;
   fa::DecodeParams p;
-  p.q = static_cast<const uint16_t*>(q);
+  p.q = rot ? reinterpret_cast<const uint16_t*>(ws) : static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k_cache);
   p.v = static_cast<const uint16_t*>(v_cache);
   p.cache_seqlens = cache_seqlens;
-  p.o_part = static_cast<float*>(workspace);
+  p.o_part = reinterpret_cast<float*>(ws + qrb);
   p.lse_part = p.o_part + rows * n_splits * head_dim;
   p.hq = heads_q;
   p.hkv = heads_kv;
@@ -243,7 +325,11 @@ fa_status fa_fwd_decode_splitkv(const void* q, const void* k_cache, const void* 
   p.n_splits = n_splits;
   p.total = (int)total;
   p.c = scale * fa::kLog2eHost;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  p.block_table = block_table;
+  p.max_blocks = max_blocks_per_seq;
+  p.page_size = page_size;
+  p.num_blocks = num_blocks;
+  p.len_add = k_new ? 1 : 0;
   hipError_t e = fa::launch_decode(p, head_dim, st);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   e = fa::launch_combine(p.o_part, p.lse_part, (int)rows, n_splits, head_dim, o, lse,

@@ -46,7 +46,7 @@ void decode_kernel(const DecodeParams p) {
   const int b = item / p.hkv;
   const int G = p.group;
   // Lengths are clamped to the cache so that a bad length cannot read past it.
-  const int Lk = min(max(p.cache_seqlens[b], 0), p.cache_len);
+  const int Lk = min(max(p.cache_seqlens[b] + p.len_add, 0), p.cache_len);
   const int kbeg = split * p.chunk;
   const int kend = min(Lk, kbeg + p.chunk);
   const size_t row0 = (size_t)b * p.hq + (size_t)kvh * G;  // output row of head kvh*G
@@ -56,9 +56,17 @@ void decode_kernel(const DecodeParams p) {
   }
 
   const size_t kv_stride = (size_t)p.hkv * D;
-  const size_t kv_off = (size_t)b * p.cache_len * kv_stride + (size_t)kvh * D;
-  const uint16_t* kbase = p.k + kv_off;
-  const uint16_t* vbase = p.v + kv_off;
+  // First row of the 128-key tile at k0 (one tile never straddles a page: the
+  // page size is a multiple of the tile and tiles start at multiples of it).
+  // Block ids are clamped to the pool so that a bad table cannot read past it.
+  auto tile_row = [&](int k0) -> size_t {
+    if (p.block_table) {
+      int blk = p.block_table[(size_t)b * p.max_blocks + k0 / p.page_size];
+      blk = min(max(blk, 0), p.num_blocks - 1);
+      return (size_t)blk * p.page_size + k0 % p.page_size;
+    }
+    return (size_t)b * p.cache_len + k0;
+  };
 
   WaveState<D, 1> st;
   st.init();
@@ -80,13 +88,16 @@ void decode_kernel(const DecodeParams p) {
   u32x4 kr[NCH], vr[NCH];
   auto load = [&](int k0) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
+    const size_t base = tile_row(k0) * kv_stride + (size_t)kvh * D;
+    const uint16_t* kt = p.k + base;
+    const uint16_t* vt = p.v + base;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = tid + i * T;
       const int key = k0 + c / CPR;
-      const size_t off = (size_t)key * kv_stride + (c % CPR) * 8;
-      kr[i] = key < kend ? *reinterpret_cast<const u32x4*>(kbase + off) : zero;
-      vr[i] = key < kend ? *reinterpret_cast<const u32x4*>(vbase + off) : zero;
+      const size_t off = (size_t)(c / CPR) * kv_stride + (c % CPR) * 8;
+      kr[i] = key < kend ? *reinterpret_cast<const u32x4*>(kt + off) : zero;
+      vr[i] = key < kend ? *reinterpret_cast<const u32x4*>(vt + off) : zero;
     }
   };
   auto store = [&]() {
@@ -167,6 +178,72 @@ void decode_kernel(const DecodeParams p) {
   }
 }
 
+// In-place append of each sequence's new token, with rotary embedding: one
+// thread per element of a query row (rotated into q_rot) or a new key row
+// (rotated, then written to cache row t = cache_seqlens[b] with the new value
+// row).  Pair i of the first rdim components turns by the angle of table row
+// t: (a, b) -> (a cos - b sin, b cos + a sin), with pairs (i, i + rdim/2) or
+// (2i, 2i + 1) when interleaved; the products and the difference are rounded
+// separately (no fused multiply-add), then the result is rounded to bf16.
+// Positions outside the table are not rotated and rows outside the cache are
+// not written (preconditions of the call; never an out-of-bounds access).
+template <int D>
+__global__ __launch_bounds__(256) void append_kernel(const AppendParams a) {
+  constexpr int RPB = 256 / D;
+  const int r = blockIdx.x * RPB + threadIdx.x / D;
+  const int e = threadIdx.x % D;
+  const int per = a.hq + a.hkv;
+  if (r >= a.batch * per) return;
+  const int b = r / per, h = r % per;
+  const bool is_q = h < a.hq;
+  if (is_q && !a.q_rot) return;
+  if (!is_q && !a.k_new) return;
+  const int t = a.cache_seqlens[b];
+  const uint16_t* src = is_q ? a.q + ((size_t)b * a.hq + h) * D
+                             : a.k_new + ((size_t)b * a.hkv + (h - a.hq)) * D;
+  auto f32 = [](uint16_t u) { return __builtin_bit_cast(float, (uint32_t)u << 16); };
+  float out = f32(src[e]);
+  if (a.cos && t >= 0 && t < a.max_pos && e < a.rdim) {
+    const int half = a.rdim / 2;
+    int i, ia, ib;
+    if (a.interleaved) {
+      i = e >> 1;
+      ia = 2 * i;
+      ib = 2 * i + 1;
+    } else {
+      i = e < half ? e : e - half;
+      ia = i;
+      ib = i + half;
+    }
+    const float x = f32(src[ia]), y = f32(src[ib]);
+    const float cs = a.cos[(size_t)t * half + i], sn = a.sin[(size_t)t * half + i];
+    {
+#pragma clang fp contract(off)
+      const float p1 = (e == ia ? x : y) * cs;
+      const float p2 = (e == ia ? y : x) * sn;
+      out = e == ia ? p1 - p2 : p1 + p2;
+    }
+  }
+  const uint16_t bits = __builtin_bit_cast(uint16_t, (__bf16)out);
+  if (is_q) {
+    a.q_rot[((size_t)b * a.hq + h) * D + e] = bits;
+    return;
+  }
+  if (t < 0 || t >= a.cache_len) return;
+  size_t row;
+  if (a.block_table) {
+    int blk = a.block_table[(size_t)b * a.max_blocks + t / a.page_size];
+    blk = min(max(blk, 0), a.num_blocks - 1);
+    row = (size_t)blk * a.page_size + t % a.page_size;
+  } else {
+    row = (size_t)b * a.cache_len + t;
+  }
+  const int kvh = h - a.hq;
+  const size_t dst = (row * a.hkv + kvh) * D + e;
+  a.k_cache[dst] = bits;
+  a.v_cache[dst] = a.v_new[((size_t)b * a.hkv + kvh) * D + e];
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
@@ -232,6 +309,18 @@ template __global__ void combine_kernel<128>(const float*, const float*, int, in
                                              int);
 template __global__ void combine_kernel<64>(const float*, const float*, int, int, void*, float*,
                                             int);
+
+hipError_t launch_append(const AppendParams& a, int head_dim, hipStream_t stream) {
+  const long long rows = (long long)a.batch * (a.hq + a.hkv);
+  const int rpb = 256 / head_dim;
+  const unsigned blocks = (unsigned)((rows + rpb - 1) / rpb);
+  if (blocks == 0) return hipSuccess;
+  if (head_dim == 128)
+    hipLaunchKernelGGL(append_kernel<128>, dim3(blocks), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(append_kernel<64>, dim3(blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream) {
   if (head_dim == 128)

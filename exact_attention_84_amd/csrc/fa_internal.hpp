@@ -48,11 +48,33 @@ struct DecodeParams {
   float* o_part;    // [B*Hq][n_splits][D]
   float* lse_part;  // [B*Hq][n_splits]
   int hq, hkv, group;
-  int cache_len;
+  int cache_len;    // rows per sequence (capacity)
   int chunk;
   int n_splits;
   int total;  // B * Hkv * n_splits
   float c;
+  // paged cache (block_table != nullptr): [num_blocks][page_size][Hkv][D],
+  // logical row j of sequence b in block block_table[b * max_blocks + j / page_size]
+  const int32_t* block_table;
+  int max_blocks, page_size, num_blocks;
+  int len_add;  // keys attended = cache_seqlens[b] + len_add (1 after an append)
+};
+
+// In-place append of one new token per sequence with rotary embedding.
+struct AppendParams {
+  const uint16_t* q;      // [B][Hq][D]
+  const uint16_t* k_new;  // [B][Hkv][D] or nullptr
+  const uint16_t* v_new;
+  uint16_t* q_rot;        // [B][Hq][D] or nullptr (no rotary)
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  const int32_t* cache_seqlens;
+  const int32_t* block_table;
+  int max_blocks, page_size, num_blocks;
+  const float* cos;       // [max_pos][rdim / 2] or nullptr
+  const float* sin;
+  int rdim, max_pos, interleaved;
+  int batch, hq, hkv, cache_len;
 };
 
 // Waves per prefill workgroup: 8 (256 query rows, half the K/V loads per
@@ -97,6 +119,7 @@ int fwd_waves(int head_dim, bool varlen, int seqlen_q);
 int fwd_block_rows(int waves);
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_append(const AppendParams& a, int head_dim, hipStream_t stream);
 hipError_t launch_combine(const float* o_part, const float* lse_part, int rows, int n_splits,
                           int head_dim, void* o, float* lse, int o_f32, hipStream_t stream);
 

@@ -131,6 +131,72 @@ fa_status fa_fwd_decode_splitkv(const void* q, const void* k_cache, const void* 
                                 fa_dtype o_dtype, void* stream);
 
 /*
+ * fa_decode_kvcache_workspace_size -- bytes of device scratch that
+ * fa_fwd_decode_kvcache needs (a bf16 copy of the rotated queries, then the
+ * split partials); max_cache_len is the per-sequence capacity.  Returns 0
+ * for invalid sizes.  A call without rotary needs only
+ * fa_decode_workspace_size(...) bytes.
+ */
+size_t fa_decode_kvcache_workspace_size(int batch, int heads_q, int max_cache_len,
+                                        int head_dim, int chunk);
+
+/*
+ * fa_fwd_decode_kvcache -- one decode step against a KV cache that the call
+ * updates in place, with rotary embedding applied to the new token in the
+ * same call and the cache optionally paged ("FlashAttention — IO 感知的精确注
+ * 意力 kernel", section 1: the KV-cache capability row (in-place append,
+ * paged KV, split-KV decode) and the usage snippet's KV-cache call).  For
+ * each sequence b, with t = cache_seqlens[b] tokens cached before the call:
+ *   1. rotary (rotary_cos != NULL): q[b] and k_new[b] are rotated at
+ *      position t.  Pair i of the first rotary_dim components, (i,
+ *      i + rotary_dim/2) or (2i, 2i + 1) when rotary_interleaved, turns by
+ *      the angle of table row t: (a, b) -> (a cos - b sin, b cos + a sin),
+ *      computed in fp32 (products and sum rounded separately) and rounded to
+ *      bf16.  q itself is not modified; the rotated copy is kept in the
+ *      workspace.
+ *   2. append (k_new != NULL): the (rotated) k_new[b] and v_new[b] are
+ *      written to cache row t of sequence b.
+ *   3. single-query attention over cache rows [0, t + (k_new != NULL)),
+ *      split into chunks and merged as in fa_fwd_decode_splitkv.
+ * cache_seqlens is read, never written: the caller advances it.
+ *
+ *   q, o             : [batch, heads_q, head_dim] bf16 / o_dtype
+ *   k_new, v_new     : [batch, heads_kv, head_dim] bf16, or both NULL
+ *   cache (block_table == NULL): k_cache, v_cache [batch, max_cache_len,
+ *                      heads_kv, head_dim] bf16
+ *   cache (paged): k_cache, v_cache [num_blocks, page_size, heads_kv,
+ *                      head_dim]; block_table device int32 [batch,
+ *                      max_blocks_per_seq]; logical row j of sequence b is
+ *                      row j % page_size of block
+ *                      block_table[b * max_blocks_per_seq + j / page_size].
+ *                      page_size is a positive multiple of 128 and
+ *                      max_cache_len must equal max_blocks_per_seq *
+ *                      page_size.
+ *   rotary_cos, rotary_sin : device fp32 [rotary_max_pos, rotary_dim / 2],
+ *                      or both NULL; rotary_dim even, <= head_dim.
+ *   lse              : [batch, heads_q] fp32
+ *   workspace        : fa_decode_kvcache_workspace_size(batch, heads_q,
+ *                      max_cache_len, head_dim, chunk) bytes, 16-byte
+ *                      aligned; contents unspecified on return.
+ * Device-side preconditions, not validated there: t + (k_new != NULL) <=
+ * max_cache_len, t < rotary_max_pos, and every block id in [0, num_blocks).
+ * A violation gives unspecified results but no out-of-bounds access: block
+ * ids are clamped, a row outside the cache is not written, and a position
+ * outside the table is not rotated.  Enqueues the append (when rotary or
+ * k_new is given), the split kernel and the combine on `stream`.
+ */
+fa_status fa_fwd_decode_kvcache(const void* q, void* k_cache, void* v_cache,
+                                const void* k_new, const void* v_new,
+                                const int32_t* cache_seqlens, const int32_t* block_table,
+                                int max_blocks_per_seq, int page_size, int num_blocks,
+                                const float* rotary_cos, const float* rotary_sin,
+                                int rotary_dim, int rotary_max_pos, int rotary_interleaved,
+                                void* o, float* lse, int batch, int heads_q, int heads_kv,
+                                int max_cache_len, int head_dim, float scale, int chunk,
+                                void* workspace, size_t workspace_bytes, fa_dtype o_dtype,
+                                void* stream);
+
+/*
  * fa_combine -- LSE-weighted merge of partial results computed over disjoint
  * key subsets (the block merge of the PKU lecture notes "FlashAttention",
  * section 6, written with logsumexps):

@@ -80,10 +80,14 @@ def cache_row_index(b: int, j: int, block_table, page_size: int):
 
 def gather_rows(cache, b: int, n: int, block_table, page_size: int) -> np.ndarray:
     """Logical rows [0, n) of sequence b as float64 [n, Hkv, d]."""
-    rows = [cache[cache_row_index(b, j, block_table, page_size)] for j in range(n)]
-    if not rows:
+    if n == 0:
         return np.zeros((0,) + tuple(cache.shape[2:]))
-    return to_f64(np.stack(rows))
+    if block_table is None:
+        return to_f64(cache[b, :n])
+    j = np.arange(n)
+    idx = [cache_row_index(b, int(x), block_table, page_size) for x in j[::page_size]]
+    blocks = np.repeat([i[0] for i in idx], page_size)[:n]
+    return to_f64(cache[blocks, j % page_size])
 
 
 def kvcache_step(q, k_cache, v_cache, cache_seqlens, scale: float, k_new=None, v_new=None,

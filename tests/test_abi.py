@@ -132,6 +132,55 @@ def test_decode_workspace_size(lib):
     assert ws(1, 1, 100, 64, 100) == 0
 
 
+def kvc(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, kn=None, vn=None, lens=FAKE, bt=None, mb=0, page=0, nb=0,
+             cos=None, sin=None, rdim=0, mpos=0, inter=0, o=FAKE, lse=FAKE, batch=4, hq=32,
+             hkv=8, ncache=4096, d=128, scale=0.088, chunk=0, ws=FAKE, wsb=1 << 40, odt=0,
+             stream=None)
+    a.update(kw)
+    return lib.fa_fwd_decode_kvcache(a["q"], a["kc"], a["vc"], a["kn"], a["vn"], a["lens"],
+                                     a["bt"], a["mb"], a["page"], a["nb"], a["cos"], a["sin"],
+                                     a["rdim"], a["mpos"], a["inter"], a["o"], a["lse"],
+                                     a["batch"], a["hq"], a["hkv"], a["ncache"], a["d"],
+                                     a["scale"], a["chunk"], a["ws"], a["wsb"], a["odt"],
+                                     a["stream"])
+
+
+PAGED = dict(bt=FAKE, mb=16, page=256, nb=64)
+ROT = dict(cos=FAKE, sin=FAKE, rdim=128, mpos=8192)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kn=FAKE), NULL), (dict(vn=FAKE), NULL), (dict(cos=FAKE, rdim=64, mpos=10), NULL),
+    (dict(lens=None), NULL),
+    (dict(PAGED, page=100), ARG), (dict(PAGED, page=0), ARG),          # not a multiple of 128
+    (dict(PAGED, mb=0), SHAPE), (dict(PAGED, nb=0), SHAPE),
+    (dict(PAGED, mb=8), SHAPE),                                        # capacity != ncache
+    (dict(ROT, rdim=3), ARG), (dict(ROT, rdim=256), ARG), (dict(ROT, mpos=0), ARG),
+    (dict(ROT, rdim=0), ARG), (dict(inter=2), ARG),
+    (dict(d=96), HEADDIM), (dict(hq=12), GQA), (dict(odt=5), DTYPE), (dict(chunk=64), ARG),
+    (dict(ws=None), WORKSPACE), (dict(ROT, wsb=100), WORKSPACE),
+])
+def test_decode_kvcache_rejects_before_launch(lib, kw, status):
+    assert kvc(lib, **kw) == status
+    assert lib.fa_last_error().decode()
+
+
+def test_decode_kvcache_workspace_size(lib):
+    ws, plain = lib.fa_decode_kvcache_workspace_size, lib.fa_decode_workspace_size
+    # rotated queries (bf16, 256-byte aligned) ahead of the split partials
+    q_bytes = 4 * 32 * 128 * 2
+    assert ws(4, 32, 4096, 128, 512) == q_bytes + plain(4, 32, 4096, 128, 512)
+    assert ws(3, 5, 1000, 64, 256) == 2048 + plain(3, 5, 1000, 64, 256)   # 1920 -> 2048
+    assert ws(1, 1, 100, 96, 0) == 0
+
+
+def test_decode_kvcache_empty_batch_is_noop(lib):
+    # nothing to compute: validated, then FA_OK without touching a device
+    assert kvc(lib, batch=0, wsb=16) == OK
+    assert kvc(lib, batch=0, wsb=16, **PAGED, **ROT) == OK
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(op=None), NULL), (dict(lp=None), NULL), (dict(o=None), NULL), (dict(lse=None), NULL),
     (dict(d=32), HEADDIM), (dict(splits=0), SHAPE), (dict(splits=5000), SHAPE),
