@@ -226,6 +226,60 @@ def other_workloads(fa, steps, warmup):
     return res
 
 
+def kvcache_workload(fa, w, steps, warmup):
+    """The decode workload as one KV-cache step per call: the cache paged in
+    256-row blocks handed out in a shuffled order, the new token's key and
+    value appended at each sequence's position, and rotary embedding (the
+    usual 10000-base tables) on its query and key.  Sequence b holds its
+    drawn length minus one before the call, so the step attends to exactly
+    the drawn lengths.  The cache contents are seeded N(0, 1) draws made on
+    the device (their values do not affect the time).  Algorithmic bytes: the
+    attended K and V rows once, the appended rows written once, q, k_new and
+    v_new read, the rotated queries written and read back, two table rows per
+    sequence, and O and LSE."""
+    import torch
+    lens = W.workload_lengths(w, seed=0) - 1
+    page = 256
+    nblk = w.seqlen_k // page
+    rng = np.random.default_rng(0)
+    table = torch.from_numpy(
+        rng.permutation(w.batch * nblk).reshape(w.batch, nblk).astype(np.int32)).cuda()
+    g = torch.Generator(device="cuda").manual_seed(0)
+    kc = torch.empty((w.batch * nblk, page, w.heads_kv, w.head_dim), dtype=torch.bfloat16,
+                     device="cuda")
+    kc.normal_(generator=g)
+    vc = torch.empty_like(kc).normal_(generator=g)
+    q = to_dev(W.decode_q(w.batch, w.heads_q, w.head_dim, seed=0, wid=w.wid))
+    kn = torch.empty((w.batch, w.heads_kv, w.head_dim), dtype=torch.bfloat16,
+                     device="cuda").normal_(generator=g)
+    vn = torch.empty_like(kn).normal_(generator=g)
+    inv = 10000.0 ** (-torch.arange(0, w.head_dim, 2, dtype=torch.float64) / w.head_dim)
+    ang = torch.outer(torch.arange(w.seqlen_k, dtype=torch.float64), inv)
+    cos, sin = ang.cos().float().cuda(), ang.sin().float().cuda()
+    cl = torch.from_numpy(lens.astype(np.int32)).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.heads_q), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.decode_kvcache_workspace_size(w.batch, w.heads_q, w.seqlen_k,
+                                                      w.head_dim), dtype=torch.uint8,
+                     device="cuda")
+    ms = time_calls(lambda: fa.decode_kvcache(q, kc, vc, cl, k_new=kn, v_new=vn,
+                                              block_table=table, rotary_cos=cos, rotary_sin=sin,
+                                              scale=w.scale, out=o, lse=lse, workspace=ws),
+                    steps, warmup)
+    row = w.heads_kv * w.head_dim * 2
+    extra = (2 * w.batch * row                                   # appended rows written
+             + 2 * w.batch * row                                 # k_new, v_new read
+             + 2 * w.batch * w.heads_q * w.head_dim * 2          # rotated q written, read
+             + 2 * w.batch * w.head_dim * 4)                     # cos and sin rows
+    by = W.decode_bytes(w, lens + 1) + extra
+    gbs = by / (ms * 1e-3) / 1e9
+    res = {"ms": round(ms, 4), "gbs": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
+           "gbytes": round(by / 1e9, 3), "page_size": page}
+    log("decode_kvcache (paged, append, rotary)", res)
+    del kc, vc
+    return res
+
+
 def backward_workload(fa, w, steps, warmup):
     """The attention backward (preprocess, dK/dV and dQ kernels) on the
     headline workload, non-causal and causal, from the forward's own O and
@@ -477,6 +531,8 @@ def main():
     del o_nc, o_c, lse_nc, lse_c
     if not a.no_extra:
         res["other_workloads"] = other_workloads(fa, max(5, a.steps // 5), max(3, a.warmup // 5))
+        res["other_workloads"]["decode_kvcache_paged_append_rotary_b64_h32kv8_cache32k_d128"] = \
+            kvcache_workload(fa, W.WORKLOADS[5], max(5, a.steps // 5), max(3, a.warmup // 5))
         res["backward"] = {"workload": w.name, "grad_dtype": "bf16",
                            **backward_workload(fa, w, max(5, a.steps // 5),
                                                max(3, a.warmup // 5))}
