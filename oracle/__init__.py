@@ -35,3 +35,10 @@ from .kvcache import (  # noqa: F401
     rotary,
     to_bf16_rne,
 )
+from .variants import (  # noqa: F401
+    attention_ext,
+    attention_ext_varlen,
+    head_attention_ext,
+    variant_scores,
+    window_mask,
+)
