@@ -48,13 +48,19 @@ def _need(t, name, dtype, ndim=None):
 def attention(q, k, v, *, causal: bool = False, scale: float | None = None,
               cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q: int | None = None,
               max_seqlen_k: int | None = None, out=None, lse=None,
-              out_dtype=torch.bfloat16, stream=None):
+              out_dtype=torch.bfloat16, window=(-1, -1), softcap: float = 0.0,
+              alibi_slopes=None, stream=None):
     """softmax(q k^T * scale) v and its row logsumexp.
 
     Fixed length: q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] -> o [B, Nq, Hq, d],
     lse [B, Nq, Hq].  Packed (cu_seqlens_q given, int32 [n+1]): q [Tq, Hq, d],
     k/v [Tk, Hkv, d] -> o [Tq, Hq, d], lse [Tq, Hq]; max_seqlen_q/k must bound
     the sequence lengths (read from the offsets on the host when omitted).
+
+    Score variants (``fa_fwd_ext``): ``window`` = (left, right) admissible
+    keys around the aligned diagonal (negative = open), ``softcap`` > 0 caps
+    the scaled scores with tanh, ``alibi_slopes`` (fp32 [Hq] or [B, Hq]) adds
+    -slope |i + Lk - Lq - j|.
     """
     lib = load()
     varlen = cu_seqlens_q is not None
@@ -101,11 +107,30 @@ def attention(q, k, v, *, causal: bool = False, scale: float | None = None,
         _need(lse, "lse", torch.float32)
         if tuple(lse.shape) != lse_shape:
             raise ValueError(f"lse must have shape {lse_shape}")
-    st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), batch, hq, hkv, nq, nk, d,
-                    scale, int(bool(causal)), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
-                    int(max_seqlen_q), int(max_seqlen_k), _OUT_DTYPES[out_dtype],
-                    _stream_handle(stream))
-    check(st, "fa_fwd")
+    left, right = (int(window[0]), int(window[1]))
+    ext = left >= 0 or right >= 0 or softcap or alibi_slopes is not None
+    if not ext:
+        st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), batch, hq, hkv, nq, nk,
+                        d, scale, int(bool(causal)), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                        int(max_seqlen_q), int(max_seqlen_k), _OUT_DTYPES[out_dtype],
+                        _stream_handle(stream))
+        check(st, "fa_fwd")
+        return out, lse
+    astride = 0
+    if alibi_slopes is not None:
+        _need(alibi_slopes, "alibi_slopes", torch.float32)
+        if tuple(alibi_slopes.shape) == (hq,):
+            astride = 0
+        elif tuple(alibi_slopes.shape) == (batch, hq):
+            astride = hq
+        else:
+            raise ValueError("alibi_slopes must be [heads_q] or [batch, heads_q]")
+    st = lib.fa_fwd_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), batch, hq, hkv, nq, nk,
+                        d, scale, int(bool(causal)), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                        int(max_seqlen_q), int(max_seqlen_k), left, right, float(softcap),
+                        _ptr(alibi_slopes), astride, _OUT_DTYPES[out_dtype],
+                        _stream_handle(stream))
+    check(st, "fa_fwd_ext")
     return out, lse
 
 

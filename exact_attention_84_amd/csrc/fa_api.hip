@@ -100,11 +100,14 @@ const char* fa_status_string(fa_status status) {
 
 const char* fa_last_error(void) { return g_last_error; }
 
-fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
-                 int heads_q, int heads_kv, int seqlen_q, int seqlen_k, int head_dim,
-                 float scale, int causal, const int32_t* cu_seqlens_q,
-                 const int32_t* cu_seqlens_k, int max_seqlen_q, int max_seqlen_k,
-                 fa_dtype o_dtype, void* stream) {
+// Validation and parameter set-up shared by fa_fwd and fa_fwd_ext.  Returns
+// FA_OK with *empty set when there is nothing to compute.
+static fa_status fwd_setup(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k,
+                           int head_dim, float scale, int causal, const int32_t* cu_seqlens_q,
+                           const int32_t* cu_seqlens_k, int max_seqlen_q, int max_seqlen_k,
+                           fa_dtype o_dtype, bool ext, fa::FwdParams* p, bool* empty) {
+  *empty = false;
   if (!valid_head_dim(head_dim))
     return fail(FA_ERR_HEADDIM, "head_dim %d not supported (64 or 128)", head_dim);
   if (batch < 0 || heads_q <= 0 || heads_kv <= 0)
@@ -139,39 +142,84 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   }
   if ((!k || !v) && (long long)batch * rows_k > 0)
     return fail(FA_ERR_NULL, "k and v must be non-NULL");
-  if (varlen && !cu_seqlens_q) return fail(FA_ERR_NULL, "cu_seqlens_q is NULL");
-  const int waves = fa::fwd_waves(head_dim, varlen, rows_q);
-  const int br = fa::fwd_block_rows(waves);
+  const int waves = ext ? 4 : fa::fwd_waves(head_dim, varlen, rows_q);
+  const int br = ext ? fa::fwd_ext_rows() : fa::fwd_block_rows(waves);
   const long long n_qtiles = (rows_q + br - 1) / br;
   // causal query tiles are processed in pairs (heavy with light), per sequence
-  const long long n_items = causal ? (n_qtiles + 1) / 2 : n_qtiles;
+  const long long n_items = (causal && !ext) ? (n_qtiles + 1) / 2 : n_qtiles;
   const long long total = (long long)batch * heads_q * n_items;
   if (total > 0x7fffffffLL) return fail(FA_ERR_SHAPE, "too many query tiles");
-  if (total == 0) return ok();  // nothing to compute
+  if (total == 0) {
+    *empty = true;
+    return ok();  // nothing to compute
+  }
+  p->q = static_cast<const uint16_t*>(q);
+  p->k = static_cast<const uint16_t*>(k);
+  p->v = static_cast<const uint16_t*>(v);
+  p->o = o;
+  p->lse = lse;
+  p->cu_q = cu_seqlens_q;
+  p->cu_k = varlen ? (cu_seqlens_k ? cu_seqlens_k : cu_seqlens_q) : nullptr;
+  p->hq = heads_q;
+  p->hkv = heads_kv;
+  p->group = heads_q / heads_kv;
+  p->seqlen_q = seqlen_q;
+  p->seqlen_k = seqlen_k;
+  p->n_qtiles = (int)n_qtiles;
+  p->n_items = (int)n_items;
+  p->total = (int)total;
+  p->waves = waves;
+  p->c = scale * fa::kLog2eHost;
+  p->o_f32 = o_dtype == FA_DTYPE_F32;
+  return ok();
+}
 
-  fa_status s = check_device();
-  if (s != FA_OK) return s;
-
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                 int heads_q, int heads_kv, int seqlen_q, int seqlen_k, int head_dim,
+                 float scale, int causal, const int32_t* cu_seqlens_q,
+                 const int32_t* cu_seqlens_k, int max_seqlen_q, int max_seqlen_k,
+                 fa_dtype o_dtype, void* stream) {
   fa::FwdParams p;
-  p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
-  p.o = o;
-  p.lse = lse;
-  p.cu_q = cu_seqlens_q;
-  p.cu_k = varlen ? (cu_seqlens_k ? cu_seqlens_k : cu_seqlens_q) : nullptr;
-  p.hq = heads_q;
-  p.hkv = heads_kv;
-  p.group = heads_q / heads_kv;
-  p.seqlen_q = seqlen_q;
-  p.seqlen_k = seqlen_k;
-  p.n_qtiles = (int)n_qtiles;
-  p.n_items = (int)n_items;
-  p.total = (int)total;
-  p.waves = waves;
-  p.c = scale * fa::kLog2eHost;
-  p.o_f32 = o_dtype == FA_DTYPE_F32;
+  bool empty;
+  fa_status s = fwd_setup(q, k, v, o, lse, batch, heads_q, heads_kv, seqlen_q, seqlen_k,
+                          head_dim, scale, causal, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                          max_seqlen_k, o_dtype, false, &p, &empty);
+  if (s != FA_OK || empty) return s;
+  s = check_device();
+  if (s != FA_OK) return s;
   hipError_t e = fa::launch_fwd(p, head_dim, causal != 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+fa_status fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k,
+                     int head_dim, float scale, int causal, const int32_t* cu_seqlens_q,
+                     const int32_t* cu_seqlens_k, int max_seqlen_q, int max_seqlen_k,
+                     int window_left, int window_right, float softcap,
+                     const float* alibi_slopes, int alibi_batch_stride, fa_dtype o_dtype,
+                     void* stream) {
+  if (!(softcap >= 0.f) || softcap > 3.0e38f)
+    return fail(FA_ERR_ARG, "softcap must be finite and >= 0");
+  if (alibi_slopes && alibi_batch_stride != 0 && alibi_batch_stride != heads_q)
+    return fail(FA_ERR_ARG, "alibi_batch_stride must be 0 or heads_q");
+  fa::FwdParams p;
+  bool empty;
+  fa_status s = fwd_setup(q, k, v, o, lse, batch, heads_q, heads_kv, seqlen_q, seqlen_k,
+                          head_dim, scale, causal, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                          max_seqlen_k, o_dtype, true, &p, &empty);
+  if (s != FA_OK || empty) return s;
+  s = check_device();
+  if (s != FA_OK) return s;
+  fa::ExtParams x;
+  x.left = window_left < 0 ? -1 : window_left;
+  x.right = window_right < 0 ? -1 : window_right;
+  x.causal = causal;
+  x.softcap = softcap;
+  x.alibi = alibi_slopes;
+  x.alibi_stride = alibi_slopes ? alibi_batch_stride : 0;
+  x.scale = scale;
+  hipError_t e = fa::launch_fwd_ext(p, x, head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   return ok();
 }

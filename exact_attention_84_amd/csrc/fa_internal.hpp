@@ -40,6 +40,16 @@ struct FwdParams {
   int o_f32;
 };
 
+// Score variants of the forward (sliding window, ALiBi, softcap).
+struct ExtParams {
+  int left, right;       // window bounds; negative = unbounded
+  int causal;
+  float softcap;         // 0 = off
+  const float* alibi;    // slopes [batch or 1][Hq], or nullptr
+  int alibi_stride;      // Hq (per sequence) or 0 (shared)
+  float scale;
+};
+
 struct DecodeParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -119,6 +129,9 @@ int fwd_waves(int head_dim, bool varlen, int seqlen_q);
 int fwd_block_rows(int waves);
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream);
+int fwd_ext_rows();
+hipError_t launch_fwd_ext(const FwdParams& p, const ExtParams& x, int head_dim,
+                          hipStream_t stream);
 hipError_t launch_append(const AppendParams& a, int head_dim, hipStream_t stream);
 hipError_t launch_combine(const float* o_part, const float* lse_part, int rows, int n_splits,
                           int head_dim, void* o, float* lse, int o_f32, hipStream_t stream);

@@ -93,6 +93,34 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  fa_dtype o_dtype, void* stream);
 
 /*
+ * fa_fwd_ext -- fa_fwd with the score variants the code-reading page lists as
+ * compile-time switches beside causal masking ("FlashAttention — IO 感知的精
+ * 确注意力 kernel", section 1 capability table: sliding window, ALiBi,
+ * softcap).  Same tensors, layouts and rules as fa_fwd.  For query i and key
+ * j of a sequence, with delta = Lk - Lq:
+ *   x = scale * <q_i, k_j>
+ *   softcap > 0          : x = softcap * tanh(x / softcap)
+ *   alibi_slopes != NULL : x = x - slope[h] * |i + delta - j|
+ *   admissible keys      : 0 <= j < Lk, j >= i + delta - window_left when
+ *                          window_left >= 0, j <= i + delta + window_right
+ *                          when window_right >= 0, and j <= i + delta when
+ *                          causal (a negative window bound is open)
+ *   O_i = softmax of x over the admissible keys, times V; lse natural log;
+ *   a row without admissible keys gets O = 0 and lse = -inf.
+ *   alibi_slopes        : device float32 [heads_q] (alibi_batch_stride = 0)
+ *                         or [batch, heads_q] (alibi_batch_stride = heads_q).
+ * Runs a separate kernel that visits only the key tiles holding admissible
+ * keys; with no variant set it equals fa_fwd (which is faster for that case).
+ */
+fa_status fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k,
+                     int head_dim, float scale, int causal,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                     int max_seqlen_q, int max_seqlen_k, int window_left, int window_right,
+                     float softcap, const float* alibi_slopes, int alibi_batch_stride,
+                     fa_dtype o_dtype, void* stream);
+
+/*
  * fa_decode_workspace_size -- bytes of float32 scratch that
  * fa_fwd_decode_splitkv needs for these sizes (partial O and LSE of every
  * key chunk).  chunk = 0 selects the built-in chunk size.  Returns 0 for

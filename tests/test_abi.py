@@ -94,6 +94,33 @@ def test_fwd_null_keys_rejected_when_keys_exist(lib):
     assert fwd(lib, nk=0, k=None, v=None, batch=0) == OK
 
 
+def fwd_ext(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, batch=2, hq=8, hkv=2, nq=16, nk=16, d=128,
+             scale=0.088, causal=0, cuq=None, cuk=None, mq=0, mk=0, left=4, right=4, cap=0.0,
+             alibi=None, astride=0, odt=0, stream=None)
+    a.update(kw)
+    return lib.fa_fwd_ext(a["q"], a["k"], a["v"], a["o"], a["lse"], a["batch"], a["hq"],
+                          a["hkv"], a["nq"], a["nk"], a["d"], a["scale"], a["causal"], a["cuq"],
+                          a["cuk"], a["mq"], a["mk"], a["left"], a["right"], a["cap"],
+                          a["alibi"], a["astride"], a["odt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cap=-1.0), ARG), (dict(cap=float("nan")), ARG), (dict(cap=float("inf")), ARG),
+    (dict(alibi=FAKE, astride=3), ARG),
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(d=96), HEADDIM), (dict(hkv=3), GQA),
+    (dict(scale=0.0), ARG), (dict(causal=2), ARG), (dict(odt=7), DTYPE), (dict(nq=-1), SHAPE),
+])
+def test_fwd_ext_rejects_before_launch(lib, kw, status):
+    assert fwd_ext(lib, **kw) == status
+    assert lib.fa_last_error().decode()
+
+
+def test_fwd_ext_empty_inputs_are_noops(lib):
+    assert fwd_ext(lib, batch=0) == OK
+    assert fwd_ext(lib, nq=0, q=None, o=None, lse=None, alibi=FAKE, astride=8) == OK
+
+
 def dec(lib, **kw):
     a = dict(q=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, o=FAKE, lse=FAKE, batch=4, hq=32, hkv=8,
              ncache=4096, d=128, scale=0.088, chunk=0, ws=FAKE, wsb=1 << 40, odt=0, stream=None)
