@@ -280,6 +280,33 @@ def kvcache_workload(fa, w, steps, warmup):
     return res
 
 
+def window_workload(fa, w, steps, warmup):
+    """The long causal GQA workload through the score-variant kernel: a
+    4096-key causal sliding window, then the same window with ALiBi slopes
+    (2^(-8 h / Hq)) and a softcap of 30.  Algorithmic flops: 4 d per
+    admissible (query, key) pair, i.e. 4 d Hq sum_i min(i + 1, 4096)."""
+    import torch
+    inp = W.make_workload(w, seed=0)
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+    win = 4096
+    pairs = sum(min(i + 1, win) for i in range(w.seqlen_q))
+    fl = 4.0 * w.head_dim * w.heads_q * w.batch * pairs
+    slopes = (2.0 ** (-8.0 * torch.arange(1, w.heads_q + 1) / w.heads_q)).float().cuda()
+    res = {}
+    for name, kw in (("window4096", {}), ("window4096_alibi_softcap30",
+                                          dict(alibi_slopes=slopes, softcap=30.0))):
+        ms = time_calls(lambda: fa.attention(q, k, v, causal=True, scale=w.scale,
+                                             window=(win - 1, 0), out=o, lse=lse, **kw),
+                        steps, warmup)
+        tf = fl / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                     "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "gflop": round(fl / 1e9, 1)}
+        log("sliding window", w.name, name, res[name])
+    return res
+
+
 def backward_workload(fa, w, steps, warmup):
     """The attention backward (preprocess, dK/dV and dQ kernels) on the
     headline workload, non-causal and causal, from the forward's own O and
@@ -533,6 +560,8 @@ def main():
         res["other_workloads"] = other_workloads(fa, max(5, a.steps // 5), max(3, a.warmup // 5))
         res["other_workloads"]["decode_kvcache_paged_append_rotary_b64_h32kv8_cache32k_d128"] = \
             kvcache_workload(fa, W.WORKLOADS[5], max(5, a.steps // 5), max(3, a.warmup // 5))
+        res["other_workloads"]["gqa_causal_b1_h32kv8_n8192_d128_sliding_window"] = \
+            window_workload(fa, W.WORKLOADS[3], max(5, a.steps // 5), max(3, a.warmup // 5))
         res["backward"] = {"workload": w.name, "grad_dtype": "bf16",
                            **backward_workload(fa, w, max(5, a.steps // 5),
                                                max(3, a.warmup // 5))}
