@@ -211,6 +211,15 @@ fa_status fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float
   if (s != FA_OK || empty) return s;
   s = check_device();
   if (s != FA_OK) return s;
+  // A window alone runs on the pipelined forward (its local-window instance);
+  // ALiBi or a softcap need the variant kernel's per-score arithmetic.
+  if (softcap == 0.f && !alibi_slopes) {
+    hipError_t e = fa::launch_fwd_local(p, head_dim, causal != 0, window_left < 0 ? -1 : window_left,
+                                        window_right < 0 ? -1 : window_right,
+                                        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+    return ok();
+  }
   fa::ExtParams x;
   x.left = window_left < 0 ? -1 : window_left;
   x.right = window_right < 0 ? -1 : window_right;

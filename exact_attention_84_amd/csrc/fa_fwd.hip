@@ -38,6 +38,20 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[NKT][NT], const int (&lim)
         if ((v & 3) + 8 * (v >> 2) + 32 * kt > lim[t]) s[kt][t][v] = -INFINITY;
 }
 
+// Sets to -inf every score of a 64-key tile whose key lies before the lane's
+// first admissible key (a local window's left edge): key offset minus 4 hh
+// below lo[t].
+template <int NT, int NKT>
+__device__ __forceinline__ void mask_tile_lo(f32x16 (&s)[NKT][NT], const int (&lo)[NT]) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if ((v & 3) + 8 * (v >> 2) + 32 * kt < lo[t]) s[kt][t][v] = -INFINITY;
+}
+
 // One steady-state step of a wave owning NT groups of 32 query rows, 64-key
 // tiles:
 //   s      = Q K_j^T            (D/8 K fragments, NT MFMAs each)
@@ -49,12 +63,13 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[NKT][NT], const int (&lim)
 // whether a row moved its reference (alpha then holds the rescale factors).
 // A tile that crosses the end of the keys or the diagonal is masked first
 // (`masked`, uniform over the wave; limits as in mask_tile).
-template <int D, int NT>
+template <int D, int NT, bool LOCAL>
 __device__ __forceinline__ bool steady_step(WaveState<D, NT>& st, const char* __restrict__ k_cur,
                                             const char* __restrict__ v_prev, const LdsRead<D>& rd,
                                             const bf16x8 (&pin)[2][NT][2],
                                             bf16x8 (&pout)[2][NT][2], float (&alpha)[NT],
-                                            float c, bool masked, const int (&lim)[NT]) {
+                                            float c, bool masked, const int (&lim)[NT],
+                                            const int (&lo)[NT]) {
   constexpr int DT = D / 32;
   constexpr int SLOTS = D / 8;                  // V fragments per step
   constexpr int LEAD = 2;                       // P V MFMAs before the first slice
@@ -65,7 +80,10 @@ __device__ __forceinline__ bool steady_step(WaveState<D, NT>& st, const char* __
 
   f32x16 s[2][NT];
   scores_tile<D, NT, 2>(s, k_cur, rd, st.qf);
-  if (masked) mask_tile<NT, 2>(s, lim);
+  if (masked) {
+    mask_tile<NT, 2>(s, lim);
+    if constexpr (LOCAL) mask_tile_lo<NT, 2>(s, lo);
+  }
 
   float mx[NT], msub[NT], rs[NT], mref[NT];
   uint32_t pk[NT][16];
@@ -143,9 +161,12 @@ __device__ __forceinline__ bool steady_step(WaveState<D, NT>& st, const char* __
 // Two waves per SIMD (256 registers each) when a wave owns 32 query rows, so
 // that one wave's MFMAs overlap the other's softmax arithmetic.  NW is 4 or 8
 // (fwd_waves); PAIR runs two causal query tiles per workgroup.
-template <int D, int NW, int NT, bool CAUSAL, bool PAIR>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
-void fwd_kernel(const FwdParams p) {
+//
+// LOCAL adds a local window: query i sees keys i + delta - left .. i + delta +
+// right (a negative bound open), visited from the workgroup's first window
+// tile on; tiles that cross a row's left edge are masked like edge tiles.
+template <int D, int NW, int NT, bool CAUSAL, bool PAIR, bool LOCAL>
+__device__ __forceinline__ void fwd_body(const FwdParams& p, int win_left, int win_right) {
   constexpr int BC = 64;
   constexpr int NKT = BC / 32;
   constexpr int BR = NW * 32 * NT;
@@ -191,16 +212,31 @@ void fwd_kernel(const FwdParams p) {
   const int q0 = qt * BR;
 
   const int delta = Lk - Lq;  // bottom-right causal offset
+  // LOCAL: right edge offset of the window (causal caps it at 0; -1 = none)
+  const int right = !LOCAL ? -1 : (CAUSAL ? (win_right < 0 ? 0 : min(win_right, 0)) : win_right);
+  // first key of query i's window (LOCAL with a left edge), else 0
+  auto key_lo = [&](int i) { return (LOCAL && win_left >= 0) ? max(0, i + delta - win_left) : 0; };
+  // Tiles kt0 .. kt0 + n_kt - 1 are visited; step j works on tile kt0 + j.
+  const int kt0 = LOCAL ? min(key_lo(q0), Lk) / BC : 0;
   int n_kt = (Lk + BC - 1) / BC;
-  if (CAUSAL) {
+  if (!LOCAL && CAUSAL) {
     const int last_key = min(Lk - 1, q0 + BR - 1 + delta);
     n_kt = last_key < 0 ? 0 : min(n_kt, last_key / BC + 1);
   }
+  if (LOCAL && right >= 0) {
+    const int last_key = min(Lk - 1, q0 + BR - 1 + delta + right);
+    n_kt = last_key < 0 ? 0 : min(n_kt, last_key / BC + 1);
+  }
+  if constexpr (LOCAL) n_kt = max(0, n_kt - kt0);
   const int qw0 = q0 + wave * 32 * NT;
   const bool wave_active = qw0 < Lq;
-  const int wave_last_key = CAUSAL ? min(Lk - 1, qw0 + 32 * NT - 1 + delta) : Lk - 1;
+  const int wave_last_key =
+      !LOCAL ? (CAUSAL ? min(Lk - 1, qw0 + 32 * NT - 1 + delta) : Lk - 1)
+             : (right >= 0 ? min(Lk - 1, qw0 + 32 * NT - 1 + delta + right) : Lk - 1);
   // Key tiles this wave needs (causal: up to its own diagonal).
-  const int wn = (wave_active && wave_last_key >= 0) ? min(n_kt, wave_last_key / BC + 1) : 0;
+  const int wn = !LOCAL ? ((wave_active && wave_last_key >= 0) ? min(n_kt, wave_last_key / BC + 1) : 0)
+                        : ((wave_active && wave_last_key >= kt0 * BC)
+                               ? min(n_kt, wave_last_key / BC + 1 - kt0) : 0);
 
   const size_t q_stride = (size_t)p.hq * D;
   const size_t kv_stride = (size_t)p.hkv * D;
@@ -211,7 +247,7 @@ void fwd_kernel(const FwdParams p) {
   dma.init(kv_stride, wave, lane);
   LdsRead<D> rd;
   rd.init(lane);
-  if (n_kt > 0) dma.issue(kbase, kv_stride, 0, Lk - 1, k_lds0, wave, lane);
+  if (n_kt > 0) dma.issue(kbase, kv_stride, kt0 * BC, Lk - 1, k_lds0, wave, lane);
 
   WaveState<D, NT> st;
   st.init();
@@ -230,7 +266,10 @@ void fwd_kernel(const FwdParams p) {
   // Score tile j needs a mask when it crosses the end of the keys or (causal)
   // this wave's diagonal; both only grow with j.
   auto edge_tile = [&](int j) {
-    const int k0 = j * BC;
+    const int k0 = (kt0 + j) * BC;
+    if constexpr (LOCAL)
+      return (k0 + BC > Lk) || (right >= 0 && k0 + BC - 1 > qw0 + delta + right) ||
+             (k0 < key_lo(qw0 + 32 * NT - 1));
     return (k0 + BC > Lk) || (CAUSAL && k0 + BC - 1 > qw0 + delta);
   };
   // Last admissible key of each of this lane's query rows, min(Lk - 1,
@@ -240,17 +279,25 @@ void fwd_kernel(const FwdParams p) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int qi = qw0 + t * 32 + m32;
-    row_lim[t] = (CAUSAL ? min(Lk - 1, qi + delta) : Lk - 1) - 4 * hh;
+    if constexpr (LOCAL)
+      row_lim[t] = (right >= 0 ? min(Lk - 1, qi + delta + right) : Lk - 1) - 4 * hh;
+    else
+      row_lim[t] = (CAUSAL ? min(Lk - 1, qi + delta) : Lk - 1) - 4 * hh;
   }
+  // LOCAL: first admissible key of each of this lane's rows, minus 4 hh
+  int row_lo[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) row_lo[t] = key_lo(qw0 + t * 32 + m32) - 4 * hh;
   // Step j: K_j and V_{j-1} are in LDS; K_{j+1} and V_j start streaming into
   // the stages that K_{j-1} and V_{j-2} used.
   auto stage = [&](int j) {
     wait_dma();       // this wave's share of K_j and V_{j-1} has landed
     __syncthreads();  // everyone's has, and everyone is done with K_{j-1}, V_{j-2}
     if (j + 1 < n_kt)
-      dma.issue(kbase, kv_stride, (j + 1) * BC, Lk - 1, (j & 1) ? k_lds0 : k_lds1, wave, lane);
+      dma.issue(kbase, kv_stride, (kt0 + j + 1) * BC, Lk - 1, (j & 1) ? k_lds0 : k_lds1, wave,
+                lane);
     if (j < n_kt)
-      dma.issue(vbase, kv_stride, j * BC, Lk - 1, (j & 1) ? v_lds1 : v_lds0, wave, lane);
+      dma.issue(vbase, kv_stride, (kt0 + j) * BC, Lk - 1, (j & 1) ? v_lds1 : v_lds0, wave, lane);
   };
 
   // The O rescale of tile j (alpha_j, when some row moved its reference) must
@@ -275,8 +322,14 @@ void fwd_kernel(const FwdParams p) {
       if (edge_tile(j)) {
         int lim[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) lim[t] = row_lim[t] - j * BC;
+        for (int t = 0; t < NT; ++t) lim[t] = row_lim[t] - (kt0 + j) * BC;
         mask_tile<NT, NKT>(s, lim);
+        if constexpr (LOCAL) {
+          int lo[NT];
+#pragma unroll
+          for (int t = 0; t < NT; ++t) lo[t] = row_lo[t] - (kt0 + j) * BC;
+          mask_tile_lo<NT, NKT>(s, lo);
+        }
       }
       moved = softmax_probs<D, NT, NKT>(st, s, p_a, alpha, p.c);
     }
@@ -293,10 +346,14 @@ void fwd_kernel(const FwdParams p) {
                     bf16x8 (&pout)[NKT][NT][2]) {
     stage(jj);
     if (__any(moved)) rescale_o<D, NT>(st, alpha);
-    int lim[NT];
+    int lim[NT], lo[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) lim[t] = row_lim[t] - jj * BC;
-    moved = steady_step<D, NT>(st, k_cur, v_prev, rd, pin, pout, alpha, p.c, edge_tile(jj), lim);
+    for (int t = 0; t < NT; ++t) {
+      lim[t] = row_lim[t] - (kt0 + jj) * BC;
+      lo[t] = row_lo[t] - (kt0 + jj) * BC;
+    }
+    moved = steady_step<D, NT, LOCAL>(st, k_cur, v_prev, rd, pin, pout, alpha, p.c, edge_tile(jj),
+                                      lim, lo);
   };
   if (wn > 1) {
     general_step(0);  // softmax of S_0 -> p_a
@@ -376,6 +433,20 @@ void fwd_kernel(const FwdParams p) {
   }
 }
 
+template <int D, int NW, int NT, bool CAUSAL, bool PAIR>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
+void fwd_kernel(const FwdParams p) {
+  fwd_body<D, NW, NT, CAUSAL, PAIR, false>(p, -1, -1);
+}
+
+// A local (sliding) window on the same pipelined path: 4-wave workgroups, no
+// tile pairing (a window makes every query tile cost about the same).
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_local_kernel(const FwdParams p, int win_left, int win_right) {
+  fwd_body<D, NW, kFwdNT, CAUSAL, false, true>(p, win_left, win_right);
+}
+
 // Explicit instantiations: every kernel the dispatcher can launch is emitted
 // on both the device and the host side.
 template __global__ void fwd_kernel<128, 4, kFwdNT, false, false>(const FwdParams);
@@ -384,6 +455,10 @@ template __global__ void fwd_kernel<128, 8, kFwdNT, false, false>(const FwdParam
 template __global__ void fwd_kernel<128, 8, kFwdNT, true, true>(const FwdParams);
 template __global__ void fwd_kernel<64, 4, kFwdNT, false, false>(const FwdParams);
 template __global__ void fwd_kernel<64, 4, kFwdNT, true, true>(const FwdParams);
+template __global__ void fwd_local_kernel<128, 4, false>(const FwdParams, int, int);
+template __global__ void fwd_local_kernel<128, 4, true>(const FwdParams, int, int);
+template __global__ void fwd_local_kernel<64, 4, false>(const FwdParams, int, int);
+template __global__ void fwd_local_kernel<64, 4, true>(const FwdParams, int, int);
 
 template <int D, int NW, int NT, bool CAUSAL, bool PAIR>
 static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
@@ -402,6 +477,17 @@ template <int D, int NW>
 static hipError_t launch_dw(const FwdParams& p, bool causal, hipStream_t stream) {
   return causal ? launch_one<D, NW, kFwdNT, true, true>(p, stream)
                 : launch_one<D, NW, kFwdNT, false, false>(p, stream);
+}
+
+hipError_t launch_fwd_local(const FwdParams& p, int head_dim, bool causal, int win_left,
+                            int win_right, hipStream_t stream) {
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(p.total), dim3(256), 0, stream, p, win_left, win_right);
+    return hipGetLastError();
+  };
+  if (head_dim == 128)
+    return causal ? go(fwd_local_kernel<128, 4, true>) : go(fwd_local_kernel<128, 4, false>);
+  return causal ? go(fwd_local_kernel<64, 4, true>) : go(fwd_local_kernel<64, 4, false>);
 }
 
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, hipStream_t stream) {

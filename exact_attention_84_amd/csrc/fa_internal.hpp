@@ -129,6 +129,8 @@ int fwd_waves(int head_dim, bool varlen, int seqlen_q);
 int fwd_block_rows(int waves);
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_fwd_local(const FwdParams& p, int head_dim, bool causal, int win_left,
+                            int win_right, hipStream_t stream);
 int fwd_ext_rows();
 hipError_t launch_fwd_ext(const FwdParams& p, const ExtParams& x, int head_dim,
                           hipStream_t stream);

@@ -130,3 +130,44 @@ def test_full_size_sliding_window_sampled(fa):
                                       True, 4095, 0, 30.0, float(sl[h]))
         check_o(og[0, rows, h], xo[rows], False, f"head {h}")
         check_lse(lg[0, rows, h], xl[rows], f"head {h}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_window_only_matches_oracle(fa, causal):
+    """A window alone runs on the pipelined forward's local-window instance."""
+    import torch
+    lens = [1, 17, 300, 0, 129, 64, 65, 513]
+    say("window varlen", causal)
+    q, k, v, cu_q, cu_k = W.make_varlen(lens, lens, 4, 2, 128, seed=24, wid=WID)
+    for window in ((40, 40), (0, -1), (200, 7)):
+        o, lse = fa.attention(dev_bf16(q), dev_bf16(k), dev_bf16(v), causal=causal, scale=0.1,
+                              cu_seqlens_q=dev_i32(cu_q), cu_seqlens_k=dev_i32(cu_k),
+                              window=window, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        orf, lrf = V.attention_ext_varlen(q, k, v, cu_q, cu_k, 0.1, causal, window=window)
+        check_o(host(o), orf, False, f"varlen {window}")
+        check_lse(host(lse), lrf, f"varlen {window}")
+
+
+def test_full_size_window_only_sampled(fa):
+    """The bench's window-only launch: the long GQA workload with a 4096-key
+    causal window on the pipelined forward, checked on sampled rows."""
+    import torch
+    say("window full size")
+    inp = W.make_workload(LONG)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    o, lse = fa.attention(dev_bf16(q), dev_bf16(k), dev_bf16(v), causal=True, scale=LONG.scale,
+                          window=(4095, 0), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    og, lg = host(o), host(lse)
+    assert np.isfinite(og).all() and np.isfinite(lg).all()
+    qf = W.bf16_bits_to_f32(q).astype(np.float64)
+    kf = W.bf16_bits_to_f32(k).astype(np.float64)
+    vf = W.bf16_bits_to_f32(v).astype(np.float64)
+    g = LONG.heads_q // LONG.heads_kv
+    rows = np.array([0, 63, 64, 4095, 4096, 4100, 6000, 8191])
+    for h in (0, 17, 31):
+        xo, xl = V.head_attention_ext(qf[0, :, h], kf[0, :, h // g], vf[0, :, h // g], LONG.scale,
+                                      True, 4095, 0, 0.0, 0.0)
+        check_o(og[0, rows, h], xo[rows], False, f"head {h}")
+        check_lse(lg[0, rows, h], xl[rows], f"head {h}")
