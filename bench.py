@@ -77,7 +77,10 @@ def kernel_source_hash(unit: str = "fa_fwd.hip", csrc: str = CSRC) -> str:
             h.update(f.encode() + code_without_comments(fh.read()).encode())
     try:
         from exact_attention_84_amd import build as B
-        h.update(" ".join(B.flags() + B.SOURCE_FLAGS.get(unit, [])).encode())
+        # options as written in the build script, with the checkout's own
+        # path left out (it differs between machines)
+        opts = [o.replace(B.ROOT, "<root>") for o in B.flags() + B.SOURCE_FLAGS.get(unit, [])]
+        h.update(" ".join(opts).encode())
     except ImportError:  # pragma: no cover
         pass
     return h.hexdigest()[:16]

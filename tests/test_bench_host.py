@@ -113,3 +113,18 @@ def test_source_hash_covers_the_unit_and_its_headers_only(tmp_path):
     assert bench.kernel_source_hash("k.hip", str(src)) == h0
     (src / "a.hpp").write_text("int g2();\n")          # an included header: stale
     assert bench.kernel_source_hash("k.hip", str(src)) != h0
+
+
+def test_source_hash_does_not_depend_on_the_checkout_path(tmp_path):
+    """The same sources hash the same from another directory (the build
+    options name the checkout's include path)."""
+    import shutil
+    import subprocess
+    import sys
+    dst = tmp_path / "copy"
+    shutil.copytree(ROOT, dst, ignore=shutil.ignore_patterns(".git", "_work", "gpurun_out",
+                                                           "_build", "*.so", "__pycache__"))
+    code = "import bench; print(bench.kernel_source_hash('fa_fwd.hip'))"
+    a = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    b = subprocess.run([sys.executable, "-c", code], cwd=dst, capture_output=True, text=True)
+    assert a.stdout.strip() and a.stdout.strip() == b.stdout.strip(), (a.stderr, b.stderr)
