@@ -143,7 +143,7 @@ static fa_status fwd_setup(const void* q, const void* k, const void* v, void* o,
   if ((!k || !v) && (long long)batch * rows_k > 0)
     return fail(FA_ERR_NULL, "k and v must be non-NULL");
   const int waves = ext ? 4 : fa::fwd_waves(head_dim, varlen, rows_q);
-  const int br = ext ? fa::fwd_ext_rows() : fa::fwd_block_rows(waves);
+  const int br = fa::fwd_block_rows(waves);
   const long long n_qtiles = (rows_q + br - 1) / br;
   // causal query tiles are processed in pairs (heavy with light), per sequence
   const long long n_items = (causal && !ext) ? (n_qtiles + 1) / 2 : n_qtiles;
@@ -211,24 +211,21 @@ fa_status fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float
   if (s != FA_OK || empty) return s;
   s = check_device();
   if (s != FA_OK) return s;
-  // A window alone runs on the pipelined forward (its local-window instance);
-  // ALiBi or a softcap need the variant kernel's per-score arithmetic.
+  // Both run on the pipelined forward: a window alone on its local-window
+  // instance, ALiBi or a softcap on the instance that transforms every score
+  // (its online softmax then works on scores already in log2 units).
+  const int left = window_left < 0 ? -1 : window_left;
+  const int right = window_right < 0 ? -1 : window_right;
+  hipError_t e;
   if (softcap == 0.f && !alibi_slopes) {
-    hipError_t e = fa::launch_fwd_local(p, head_dim, causal != 0, window_left < 0 ? -1 : window_left,
-                                        window_right < 0 ? -1 : window_right,
-                                        static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
-    return ok();
+    e = fa::launch_fwd_local(p, head_dim, causal != 0, left, right,
+                             static_cast<hipStream_t>(stream));
+  } else {
+    p.c = 1.f;
+    e = fa::launch_fwd_xf(p, head_dim, causal != 0, left, right, scale, softcap, alibi_slopes,
+                          alibi_slopes ? alibi_batch_stride : 0,
+                          static_cast<hipStream_t>(stream));
   }
-  fa::ExtParams x;
-  x.left = window_left < 0 ? -1 : window_left;
-  x.right = window_right < 0 ? -1 : window_right;
-  x.causal = causal;
-  x.softcap = softcap;
-  x.alibi = alibi_slopes;
-  x.alibi_stride = alibi_slopes ? alibi_batch_stride : 0;
-  x.scale = scale;
-  hipError_t e = fa::launch_fwd_ext(p, x, head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   return ok();
 }

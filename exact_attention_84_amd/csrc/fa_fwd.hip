@@ -18,6 +18,21 @@
 // inside one wavefront): step j computes the scores of tile j, then issues the
 // P V MFMAs of tile j-1 one by one with a slice of the softmax of tile j after
 // each.
+//
+// The score variants the code-reading page lists as compile-time switches
+// next to causal masking ("FlashAttention — IO 感知的精确注意力 kernel",
+// section 1 capability table: sliding window, ALiBi, softcap) are further
+// instances of the same pipelined body.  For query i and key j of a sequence
+// (delta = Lk - Lq aligns the last query with the last key):
+//   x_ij = scale <q_i, k_j>
+//   x_ij = cap tanh(x_ij / cap)                      (softcap, cap > 0)
+//   x_ij = x_ij - slope_h |i + delta - j|            (ALiBi, slopes given)
+//   j admissible: 0 <= j < Lk, and
+//     j >= i + delta - left  (left >= 0),  j <= i + delta + right (right >= 0),
+//     j <= i + delta         (causal)
+// The local instance visits only the key tiles that hold admissible keys of
+// the workgroup's rows, so a window of w keys costs about w keys per query;
+// the transform instance adds the softcap and ALiBi to every score it forms.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -52,6 +67,54 @@ __device__ __forceinline__ void mask_tile_lo(f32x16 (&s)[NKT][NT], const int (&l
         if ((v & 3) + 8 * (v >> 2) + 32 * kt < lo[t]) s[kt][t][v] = -INFINITY;
 }
 
+// Per-score transform of the ALiBi / softcap instance: the raw score s of
+// query row qi and key kj becomes, in log2 units (L = log2 e),
+//   y = s * scale;  y = cap * tanh(y / cap) (cap > 0);  y -= slope |qi + delta - kj|
+// with tanh(x) = 1 - 2 / (exp(2x) + 1) from one exp2 and one hardware
+// reciprocal (each within an ulp or so; exp2 -> inf gives tanh = 1).  The
+// constants arrive folded: k = scale L without a cap, 2 scale L / cap with
+// one; cap_l = cap L (0: no cap); slope_l = slope L.  rel[t] is
+// qi + delta - 4 hh - k0 for the lane's row of group t and the tile's first
+// key k0, so that the distance of element (kt, v) is |rel - 32 kt - c_v|.
+struct ScoreXf {
+  float k, cap_l, slope_l;
+};
+template <int NT, int NKT>
+__device__ __forceinline__ void transform_tile(f32x16 (&s)[NKT][NT], const ScoreXf& x,
+                                               const int (&rel)[NT]) {
+  if (x.cap_l > 0.f) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float e = fast_exp2(s[kt][t][v] * x.k);
+          s[kt][t][v] = fmaf(-2.f * x.cap_l, __builtin_amdgcn_rcpf(e + 1.f), x.cap_l);
+        }
+  } else {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[kt][t][v] *= x.k;
+  }
+  if (x.slope_l != 0.f) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float r = static_cast<float>(rel[t]);  // exact: |rel| < 2^24
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float c = static_cast<float>(32 * kt + (v & 3) + 8 * (v >> 2));
+          s[kt][t][v] = fmaf(-x.slope_l, fabsf(r - c), s[kt][t][v]);
+        }
+    }
+  }
+}
+
 // One steady-state step of a wave owning NT groups of 32 query rows, 64-key
 // tiles:
 //   s      = Q K_j^T            (D/8 K fragments, NT MFMAs each)
@@ -63,13 +126,14 @@ __device__ __forceinline__ void mask_tile_lo(f32x16 (&s)[NKT][NT], const int (&l
 // whether a row moved its reference (alpha then holds the rescale factors).
 // A tile that crosses the end of the keys or the diagonal is masked first
 // (`masked`, uniform over the wave; limits as in mask_tile).
-template <int D, int NT, bool LOCAL>
+template <int D, int NT, bool LOCAL, bool XF>
 __device__ __forceinline__ bool steady_step(WaveState<D, NT>& st, const char* __restrict__ k_cur,
                                             const char* __restrict__ v_prev, const LdsRead<D>& rd,
                                             const bf16x8 (&pin)[2][NT][2],
                                             bf16x8 (&pout)[2][NT][2], float (&alpha)[NT],
                                             float c, bool masked, const int (&lim)[NT],
-                                            const int (&lo)[NT]) {
+                                            const int (&lo)[NT], const ScoreXf& xf,
+                                            const int (&rel)[NT]) {
   constexpr int DT = D / 32;
   constexpr int SLOTS = D / 8;                  // V fragments per step
   constexpr int LEAD = 2;                       // P V MFMAs before the first slice
@@ -80,6 +144,7 @@ __device__ __forceinline__ bool steady_step(WaveState<D, NT>& st, const char* __
 
   f32x16 s[2][NT];
   scores_tile<D, NT, 2>(s, k_cur, rd, st.qf);
+  if constexpr (XF) transform_tile<NT, 2>(s, xf, rel);
   if (masked) {
     mask_tile<NT, 2>(s, lim);
     if constexpr (LOCAL) mask_tile_lo<NT, 2>(s, lo);
@@ -165,8 +230,9 @@ __device__ __forceinline__ bool steady_step(WaveState<D, NT>& st, const char* __
 // LOCAL adds a local window: query i sees keys i + delta - left .. i + delta +
 // right (a negative bound open), visited from the workgroup's first window
 // tile on; tiles that cross a row's left edge are masked like edge tiles.
-template <int D, int NW, int NT, bool CAUSAL, bool PAIR, bool LOCAL>
-__device__ __forceinline__ void fwd_body(const FwdParams& p, int win_left, int win_right) {
+template <int D, int NW, int NT, bool CAUSAL, bool PAIR, bool LOCAL, bool XF = false>
+__device__ __forceinline__ void fwd_body(const FwdParams& p, int win_left, int win_right,
+                                         const ScoreXf& xf = ScoreXf{}) {
   constexpr int BC = 64;
   constexpr int NKT = BC / 32;
   constexpr int BR = NW * 32 * NT;
@@ -288,6 +354,10 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, int win_left, int w
   int row_lo[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) row_lo[t] = key_lo(qw0 + t * 32 + m32) - 4 * hh;
+  // XF: the lane's aligned diagonal position, minus 4 hh (ALiBi distances)
+  int row_rel[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) row_rel[t] = qw0 + t * 32 + m32 + delta - 4 * hh;
   // Step j: K_j and V_{j-1} are in LDS; K_{j+1} and V_j start streaming into
   // the stages that K_{j-1} and V_{j-2} used.
   auto stage = [&](int j) {
@@ -319,6 +389,12 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, int win_left, int w
     if (j < wn) {
       f32x16 s[NKT][NT];
       scores_tile<D, NT, NKT, false>(s, k_cur, rd, st.qf);
+      if constexpr (XF) {
+        int rel[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) rel[t] = row_rel[t] - (kt0 + j) * BC;
+        transform_tile<NT, NKT>(s, xf, rel);
+      }
       if (edge_tile(j)) {
         int lim[NT];
 #pragma unroll
@@ -346,14 +422,15 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, int win_left, int w
                     bf16x8 (&pout)[NKT][NT][2]) {
     stage(jj);
     if (__any(moved)) rescale_o<D, NT>(st, alpha);
-    int lim[NT], lo[NT];
+    int lim[NT], lo[NT], rel[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       lim[t] = row_lim[t] - (kt0 + jj) * BC;
       lo[t] = row_lo[t] - (kt0 + jj) * BC;
+      rel[t] = row_rel[t] - (kt0 + jj) * BC;
     }
-    moved = steady_step<D, NT, LOCAL>(st, k_cur, v_prev, rd, pin, pout, alpha, p.c, edge_tile(jj),
-                                      lim, lo);
+    moved = steady_step<D, NT, LOCAL, XF>(st, k_cur, v_prev, rd, pin, pout, alpha, p.c,
+                                          edge_tile(jj), lim, lo, xf, rel);
   };
   if (wn > 1) {
     general_step(0);  // softmax of S_0 -> p_a
@@ -447,6 +524,27 @@ void fwd_local_kernel(const FwdParams p, int win_left, int win_right) {
   fwd_body<D, NW, kFwdNT, CAUSAL, false, true>(p, win_left, win_right);
 }
 
+// The local instance with the ALiBi / softcap transform: the slope is per
+// (sequence, query head), read from alibi[b * alibi_stride + h].
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_xf_kernel(const FwdParams p, int win_left, int win_right, float scale, float cap,
+                   const float* alibi, int alibi_stride) {
+  // the slope of this workgroup's (sequence, head), found as fwd_body finds them
+  const int item = xcd_remap(blockIdx.x, p.total, p.group * p.n_items);
+  int rest = item / p.n_items;
+  const int hg = rest % p.group;
+  rest /= p.group;
+  const int kvh = rest % p.hkv;
+  const int b = rest / p.hkv;
+  const float slope = alibi ? alibi[(size_t)b * alibi_stride + kvh * p.group + hg] : 0.f;
+  ScoreXf xf;
+  xf.k = cap > 0.f ? 2.f * scale * kLog2e / cap : scale * kLog2e;
+  xf.cap_l = cap * kLog2e;
+  xf.slope_l = slope * kLog2e;
+  fwd_body<D, NW, kFwdNT, CAUSAL, false, true, true>(p, win_left, win_right, xf);
+}
+
 // Explicit instantiations: every kernel the dispatcher can launch is emitted
 // on both the device and the host side.
 template __global__ void fwd_kernel<128, 4, kFwdNT, false, false>(const FwdParams);
@@ -459,6 +557,14 @@ template __global__ void fwd_local_kernel<128, 4, false>(const FwdParams, int, i
 template __global__ void fwd_local_kernel<128, 4, true>(const FwdParams, int, int);
 template __global__ void fwd_local_kernel<64, 4, false>(const FwdParams, int, int);
 template __global__ void fwd_local_kernel<64, 4, true>(const FwdParams, int, int);
+template __global__ void fwd_xf_kernel<128, 4, false>(const FwdParams, int, int, float, float,
+                                                      const float*, int);
+template __global__ void fwd_xf_kernel<128, 4, true>(const FwdParams, int, int, float, float,
+                                                     const float*, int);
+template __global__ void fwd_xf_kernel<64, 4, false>(const FwdParams, int, int, float, float,
+                                                     const float*, int);
+template __global__ void fwd_xf_kernel<64, 4, true>(const FwdParams, int, int, float, float,
+                                                    const float*, int);
 
 template <int D, int NW, int NT, bool CAUSAL, bool PAIR>
 static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
@@ -488,6 +594,19 @@ hipError_t launch_fwd_local(const FwdParams& p, int head_dim, bool causal, int w
   if (head_dim == 128)
     return causal ? go(fwd_local_kernel<128, 4, true>) : go(fwd_local_kernel<128, 4, false>);
   return causal ? go(fwd_local_kernel<64, 4, true>) : go(fwd_local_kernel<64, 4, false>);
+}
+
+hipError_t launch_fwd_xf(const FwdParams& p, int head_dim, bool causal, int win_left,
+                         int win_right, float scale, float cap, const float* alibi,
+                         int alibi_stride, hipStream_t stream) {
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(p.total), dim3(256), 0, stream, p, win_left, win_right, scale,
+                       cap, alibi, alibi_stride);
+    return hipGetLastError();
+  };
+  if (head_dim == 128)
+    return causal ? go(fwd_xf_kernel<128, 4, true>) : go(fwd_xf_kernel<128, 4, false>);
+  return causal ? go(fwd_xf_kernel<64, 4, true>) : go(fwd_xf_kernel<64, 4, false>);
 }
 
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, hipStream_t stream) {

@@ -36,18 +36,8 @@ struct FwdParams {
                            // ceil(n_qtiles / 2) when causal tiles are paired
   int total;               // workgroups
   int waves;               // waves per workgroup (4 or 8)
-  float c;                 // scale * log2(e)
+  float c;                 // scale * log2(e); 1 where scores arrive in log2 units
   int o_f32;
-};
-
-// Score variants of the forward (sliding window, ALiBi, softcap).
-struct ExtParams {
-  int left, right;       // window bounds; negative = unbounded
-  int causal;
-  float softcap;         // 0 = off
-  const float* alibi;    // slopes [batch or 1][Hq], or nullptr
-  int alibi_stride;      // Hq (per sequence) or 0 (shared)
-  float scale;
 };
 
 struct DecodeParams {
@@ -131,9 +121,9 @@ hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, hipStream_t
 hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_fwd_local(const FwdParams& p, int head_dim, bool causal, int win_left,
                             int win_right, hipStream_t stream);
-int fwd_ext_rows();
-hipError_t launch_fwd_ext(const FwdParams& p, const ExtParams& x, int head_dim,
-                          hipStream_t stream);
+hipError_t launch_fwd_xf(const FwdParams& p, int head_dim, bool causal, int win_left,
+                         int win_right, float scale, float cap, const float* alibi,
+                         int alibi_stride, hipStream_t stream);
 hipError_t launch_append(const AppendParams& a, int head_dim, hipStream_t stream);
 hipError_t launch_combine(const float* o_part, const float* lse_part, int rows, int n_splits,
                           int head_dim, void* o, float* lse, int o_f32, hipStream_t stream);

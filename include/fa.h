@@ -109,8 +109,11 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  *   a row without admissible keys gets O = 0 and lse = -inf.
  *   alibi_slopes        : device float32 [heads_q] (alibi_batch_stride = 0)
  *                         or [batch, heads_q] (alibi_batch_stride = heads_q).
- * Runs a separate kernel that visits only the key tiles holding admissible
- * keys; with no variant set it equals fa_fwd (which is faster for that case).
+ * Runs the pipelined forward's window instance, which visits only the key
+ * tiles holding admissible keys (with ALiBi or a softcap, its instance that
+ * transforms every score); with no variant set it equals fa_fwd, which pairs
+ * causal tiles and is faster for that case.  The softcap and the distance
+ * bias are computed in fp32 (tanh from one exp2 and one reciprocal).
  */
 fa_status fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
                      int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k,

@@ -42,6 +42,8 @@ CASES = [
     (2, 250, 300, 8, 2, 64, False, (-1, -1), 0.0, "batch"),       # ALiBi slopes [B, Hq]
     (1, 520, 520, 4, 1, 128, True, (128, -1), 20.0, "head"),      # all three
     (3, 130, 130, 2, 2, 64, False, (16, 16), 10.0, "batch"),
+    (1, 300, 300, 2, 2, 128, False, (-1, -1), 0.5, None),         # cap saturates tanh
+    (1, 300, 300, 4, 2, 128, True, (-1, -1), 0.0, "steep"),       # slopes up to 32 per key
 ]
 
 
@@ -49,7 +51,8 @@ def run(fa, case, out):
     import torch
     bsz, nq, nk, hq, hkv, d, causal, window, cap, alibi = case
     q, k, v = W.make_fixed(bsz, hq, hkv, nq, nk, d, seed=21, wid=WID, k_mult=1.5)
-    sl = None if alibi is None else (slopes(hq) if alibi == "head" else slopes(hq, bsz))
+    sl = (None if alibi is None else slopes(hq) if alibi == "head" else
+          slopes(hq, bsz) if alibi == "batch" else 64 * slopes(hq))
     scale = 1.0 / np.sqrt(d)
     o, lse = fa.attention(dev_bf16(q), dev_bf16(k), dev_bf16(v), causal=causal, scale=scale,
                           window=window, softcap=cap,
