@@ -42,3 +42,11 @@ from .variants import (  # noqa: F401
     variant_scores,
     window_mask,
 )
+from .fp8 import (  # noqa: F401
+    attention_fp8,
+    attention_fp8_rounded_p,
+    dequantize,
+    e4m3_to_f64,
+    p_rounding_bound,
+    round_to_e4m3,
+)

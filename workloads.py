@@ -150,6 +150,40 @@ def make_dout(q_shape, *, seed=0, wid=0, cu_q=None) -> np.ndarray:
     return do
 
 
+# FP8 inputs: N(0,1) draws times a per-tensor multiplier, cast to E4M3 codes by
+# torch's float8_e4m3fn conversion (nearest, ties to even), with descale =
+# 1 / multiplier so that descale * decoded codes is N(0,1)-shaped (times
+# k_mult for K).  The multipliers put the bulk of each tensor in E4M3's normal
+# range; draws are clipped to +-440 first (E4M3's largest finite value is 448).
+FP8_MULT = {T_Q: 32.0, T_K: 16.0, T_V: 64.0}
+
+
+def normal_fp8(seed: int, wid: int, tensor: int, shape, slc: int = 0,
+               mult: float = 1.0) -> np.ndarray:
+    """uint8 E4M3 codes of a N(0,1) draw times ``mult`` times the tensor's
+    FP8 multiplier."""
+    import torch
+    x = _rng(seed, wid, tensor, slc).standard_normal(size=shape, dtype=np.float32)
+    x *= np.float32(mult * FP8_MULT[tensor])
+    np.clip(x, -440.0, 440.0, out=x)
+    return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def make_fixed_fp8(batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim, *, seed=0,
+                   wid=0, k_mult=1.0):
+    """q8 [B,Nq,Hq,d], k8/v8 [B,Nk,Hkv,d] as E4M3 codes plus the three
+    per-tensor descales (q, k, v); one slice per batch entry."""
+    q = np.empty((batch, seqlen_q, heads_q, head_dim), np.uint8)
+    k = np.empty((batch, seqlen_k, heads_kv, head_dim), np.uint8)
+    v = np.empty((batch, seqlen_k, heads_kv, head_dim), np.uint8)
+    for b in range(batch):
+        q[b] = normal_fp8(seed, wid, T_Q, q.shape[1:], b)
+        k[b] = normal_fp8(seed, wid, T_K, k.shape[1:], b, k_mult)
+        v[b] = normal_fp8(seed, wid, T_V, v.shape[1:], b)
+    descales = tuple(1.0 / FP8_MULT[t] for t in (T_Q, T_K, T_V))
+    return q, k, v, descales
+
+
 BF16_NAN = np.uint16(0x7FC0)
 
 
