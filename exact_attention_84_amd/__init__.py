@@ -18,7 +18,7 @@ import torch
 
 from ._lib import FA_DTYPE_BF16, FA_DTYPE_F32, FaError, check, load
 
-__all__ = ["attention", "decode", "combine", "decode_workspace_size", "FaError", "load"]
+__all__ = ["attention", "attention_fp8", "decode", "combine", "decode_workspace_size", "FaError", "load"]
 
 _OUT_DTYPES = {torch.bfloat16: FA_DTYPE_BF16, torch.float32: FA_DTYPE_F32}
 
@@ -131,6 +131,74 @@ def attention(q, k, v, *, causal: bool = False, scale: float | None = None,
                         _ptr(alibi_slopes), astride, _OUT_DTYPES[out_dtype],
                         _stream_handle(stream))
     check(st, "fa_fwd_ext")
+    return out, lse
+
+
+def _fp8_codes(t, name, ndim):
+    if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    _need(t, name, torch.uint8, ndim)
+    return t
+
+
+def attention_fp8(q, k, v, *, q_descale: float = 1.0, k_descale: float = 1.0,
+                  v_descale: float = 1.0, causal: bool = False, scale: float | None = None,
+                  cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q: int | None = None,
+                  max_seqlen_k: int | None = None, out=None, lse=None,
+                  out_dtype=torch.bfloat16, stream=None):
+    """``attention`` of FP8 inputs (``fa_fwd_fp8``): q, k, v hold E4M3 codes
+    (torch.uint8 or torch.float8_e4m3fn, same shapes as ``attention``; head
+    dim 128) and the real tensors are q_descale * q, k_descale * k and
+    v_descale * v.  Returns (o, lse) of the real tensors."""
+    lib = load()
+    varlen = cu_seqlens_q is not None
+    ndim = 3 if varlen else 4
+    q, k, v = (_fp8_codes(t, n, ndim) for t, n in ((q, "q"), (k, "k"), (v, "v")))
+    if out_dtype not in _OUT_DTYPES:
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    d = q.shape[-1]
+    if k.shape[-1] != d:
+        raise ValueError("q and k head dims differ")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if varlen:
+        _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+        if cu_seqlens_k is not None:
+            _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+        batch = cu_seqlens_q.numel() - 1
+        if max_seqlen_q is None:
+            max_seqlen_q = int(torch.diff(cu_seqlens_q).max().item()) if batch > 0 else 0
+        if max_seqlen_k is None:
+            ck = cu_seqlens_q if cu_seqlens_k is None else cu_seqlens_k
+            max_seqlen_k = int(torch.diff(ck).max().item()) if batch > 0 else 0
+        hq, hkv, nq, nk = q.shape[1], k.shape[1], 0, 0
+        lse_shape = (q.shape[0], hq)
+    else:
+        batch, nq, hq, _ = q.shape
+        nk, hkv = k.shape[1], k.shape[2]
+        if k.shape[0] != batch:
+            raise ValueError("q and k batch sizes differ")
+        max_seqlen_q = max_seqlen_k = 0
+        lse_shape = (batch, nq, hq)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    else:
+        _need(out, "out", out_dtype, ndim)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    if lse is None:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    else:
+        _need(lse, "lse", torch.float32)
+        if tuple(lse.shape) != lse_shape:
+            raise ValueError(f"lse must have shape {lse_shape}")
+    st = lib.fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), batch, hq, hkv, nq, nk,
+                        d, scale, float(q_descale), float(k_descale), float(v_descale),
+                        int(bool(causal)), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                        int(max_seqlen_q), int(max_seqlen_k), _OUT_DTYPES[out_dtype],
+                        _stream_handle(stream))
+    check(st, "fa_fwd_fp8")
     return out, lse
 
 

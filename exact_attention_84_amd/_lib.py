@@ -18,7 +18,8 @@ FA_DTYPE_F32 = 1
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM",
                 4: "FA_ERR_GQA", 5: "FA_ERR_DTYPE", 6: "FA_ERR_ARCH", 7: "FA_ERR_WORKSPACE",
                 8: "FA_ERR_HIP", 9: "FA_ERR_ARG"}
-EXPORTS = ("fa_fwd", "fa_fwd_ext", "fa_decode_workspace_size", "fa_fwd_decode_splitkv",
+EXPORTS = ("fa_fwd", "fa_fwd_ext", "fa_fwd_fp8", "fa_decode_workspace_size",
+           "fa_fwd_decode_splitkv",
            "fa_decode_kvcache_workspace_size", "fa_fwd_decode_kvcache", "fa_combine",
            "fa_bwd_workspace_size", "fa_bwd", "fa_status_string", "fa_last_error")
 
@@ -57,6 +58,8 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_ext.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, I, I, I, I, F, P, I,
                                I, P]
     lib.fa_fwd_ext.restype = I
+    lib.fa_fwd_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, F, F, F, I, P, P, I, I, I, P]
+    lib.fa_fwd_fp8.restype = I
     lib.fa_decode_kvcache_workspace_size.argtypes = [I, I, I, I, I]
     lib.fa_decode_kvcache_workspace_size.restype = ctypes.c_size_t
     lib.fa_fwd_decode_kvcache.argtypes = [P, P, P, P, P, P, P, I, I, I, P, P, I, I, I, P, P, I, I,

@@ -192,6 +192,33 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   return ok();
 }
 
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k,
+                     int head_dim, float scale, float q_descale, float k_descale,
+                     float v_descale, int causal, const int32_t* cu_seqlens_q,
+                     const int32_t* cu_seqlens_k, int max_seqlen_q, int max_seqlen_k,
+                     fa_dtype o_dtype, void* stream) {
+  if (head_dim != 128)
+    return fail(FA_ERR_HEADDIM, "the FP8 forward supports head_dim 128 (got %d)", head_dim);
+  if (!valid_scale(q_descale) || !valid_scale(k_descale) || !valid_scale(v_descale))
+    return fail(FA_ERR_ARG, "descales must be finite and > 0");
+  fa::FwdParams p;
+  bool empty;
+  fa_status s = fwd_setup(q, k, v, o, lse, batch, heads_q, heads_kv, seqlen_q, seqlen_k,
+                          head_dim, scale, causal, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                          max_seqlen_k, o_dtype, false, &p, &empty);
+  if (s != FA_OK || empty) return s;
+  const float c = scale * q_descale * k_descale * fa::kLog2eHost;
+  if (!isfinite(c) || !(c > 0.f)) return fail(FA_ERR_ARG, "scale * q_descale * k_descale out of range");
+  p.c = c;
+  s = check_device();
+  if (s != FA_OK) return s;
+  hipError_t e =
+      fa::launch_fwd_fp8(p, causal != 0, v_descale, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "FP8 forward launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 fa_status fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
                      int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k,
                      int head_dim, float scale, int causal, const int32_t* cu_seqlens_q,

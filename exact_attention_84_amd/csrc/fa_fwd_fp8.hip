@@ -1,0 +1,363 @@
+// FP8 attention forward: both matrix products on gfx950's FP8 matrix cores
+// (the FlashAttention 3 low-precision item of "推理优化 | FlashAttention 1-4
+// 详解", section FlashAttention 3 的硬件特性利用: the forward's products in
+// FP8, the backward in BF16).  Q, K and V arrive as OCP E4M3 codes with one
+// fp32 descale per tensor (real value = descale * code value); the result is
+// attention of the real tensors, with O in bf16 or fp32 and the natural-log
+// LSE in fp32.
+//
+// Same decomposition as the bf16 forward (a workgroup per query tile of BR =
+// 32 NW rows of one (sequence, query head), causal tiles paired heavy with
+// light, Q in registers, K/V tiles of 64 keys streamed into LDS by direct
+// loads, online softmax in base 2 with a lazy reference), with the FP8 data
+// path:
+//   * S^T = K Q^T with v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales):
+//     2 k-steps of 64 head-dim values per 32-key sub-tile;
+//   * the descales fold into the softmax constant c = scale dq dk log2 e, and
+//     dv multiplies O at the end;
+//   * P = exp2(s c - r) <= 2^8 (the lazy reference stays within 8 of the row
+//     maximum) is rounded to E4M3 (v_cvt_pk_fp8_f32, nearest-even; 256 < 448
+//     never saturates) straight from the accumulators into the B operand of
+//     O^T = V^T P^T; the row sum l adds the unrounded values;
+//   * V^T comes from the row-major V tile with transposing byte reads
+//     (ds_read_b64_tr_b8), one MFMA of 64 keys per 32 head-dim rows.
+// The LDS layouts, and which key each operand slot holds, are those of
+// fa_layout.hpp (k8_*, v8_*, pv8_key).
+#include "fa_device.hpp"
+#include "fa_internal.hpp"
+
+namespace fa {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD8 = 128;              // head dim
+constexpr int kBC8 = 64;              // keys per tile
+constexpr int kTile8 = kBC8 * kD8;    // bytes per K or V tile
+
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Direct global->LDS fill of one 64-row FP8 tile: 8 wave instructions of
+// 64 x 16 bytes, NW waves issuing 8 / NW each.  Rows past klast are read from
+// row klast (their scores are masked, so they only meet zero probabilities).
+template <int NW, bool V_TILE>
+struct Dma8 {
+  static constexpr int PER_WAVE = 8 / NW;
+  static_assert(8 % NW == 0, "tile instructions must split evenly over the waves");
+  int off[PER_WAVE];
+
+  __device__ __forceinline__ void init(int row_stride, int wave, int lane) {
+#pragma unroll
+    for (int n = 0; n < PER_WAVE; ++n) {
+      const int inst = wave + n * NW;
+      off[n] = dma8_row(inst, lane) * row_stride + (dma8_chunk(inst, lane, V_TILE) << 4);
+    }
+  }
+  __device__ __forceinline__ void issue(const uint8_t* __restrict__ base, int row_stride, int k0,
+                                        int klast, char* lds, int wave, int lane) const {
+    const uint8_t* tile = base + (size_t)k0 * row_stride;
+    if (k0 + kBC8 - 1 <= klast) {
+#pragma unroll
+      for (int n = 0; n < PER_WAVE; ++n)
+        __builtin_amdgcn_global_load_lds(tile + off[n], (lds_void*)(lds + (wave + n * NW) * 1024),
+                                         16, 0, 0);
+    } else {
+#pragma unroll
+      for (int n = 0; n < PER_WAVE; ++n) {
+        const int inst = wave + n * NW;
+        const int src = min(k0 + dma8_row(inst, lane), klast);
+        const uint8_t* g =
+            base + (size_t)src * row_stride + (dma8_chunk(inst, lane, V_TILE) << 4);
+        __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds + inst * 1024), 16, 0, 0);
+      }
+    }
+  }
+};
+
+// Per-lane LDS offsets of the operand reads.
+struct Rd8 {
+  uint32_t kb[2][2];  // K: [k-step][16-byte half], key rows 0..31
+  uint32_t vb[4];     // V^T: [head-dim block], read q = 0
+
+  __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) kb[st][u] = k8_read_offset(lane, st, u);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) vb[dt] = v8_read_offset(lane, dt);
+  }
+  // A operand of S^T = K Q^T: keys 32 kt.., head-dim 64 st + 32 hh ..
+  __device__ __forceinline__ i32x8 k(const char* __restrict__ lds, int kt, int st) const {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(lds + kb[st][0] + kt * 32 * kD8);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(lds + kb[st][1] + kt * 32 * kD8);
+    const i32x8 r = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    return r;
+  }
+  // A operand of O^T = V^T P^T for head-dim rows 32 dt..: four transposing
+  // reads, read q filling slots 8 q .. 8 q + 7.
+  __device__ __forceinline__ i32x8 v(const char* __restrict__ lds, int dt) const {
+    i32x8 r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) i32x2*)(lds + vb[dt] + 2048 * q));
+      r[2 * q] = w[0];
+      r[2 * q + 1] = w[1];
+    }
+    return r;
+  }
+};
+
+struct State8 {
+  i32x8 qf[2];     // Q^T, B operand of S^T = K Q^T, per k-step
+  f32x16 o[4];     // O^T accumulators (unnormalised), per 32 head-dim rows
+  float mc;        // reference, in units of c (log2)
+  float l;         // row sum of this half-wave's keys, relative to mc
+};
+
+// Online-softmax step for one 64-key tile: new reference, rescale factor,
+// probabilities rounded to E4M3 into the B operand (slot 16 kt + v holds
+// element v of sub-tile kt).  Returns whether the row moved its reference.
+__device__ __forceinline__ bool softmax8(State8& st, f32x16 (&s)[2], i32x8& pb, float& alpha,
+                                         float c) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt][v]);
+  const float mx_c = halfwave_max(mx) * c;
+  const float mref = (mx_c > st.mc + kRescaleTau) ? mx_c : st.mc;
+  const bool moved = mref != st.mc;
+  // a row that has seen only masked keys keeps -inf; subtract 0 then
+  const float msub = (mref == -INFINITY) ? 0.f : mref;
+  alpha = fast_exp2(st.mc - msub);
+  float rs = 0.f;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    float pr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = 4 * w + e;
+      pr[e] = fast_exp2(fmaf(s[idx >> 4][idx & 15], c, -msub));
+      rs += pr[e];
+    }
+    int x = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
+    x = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], x, true);
+    pb[w] = x;
+  }
+  st.l = fmaf(alpha, st.l, rs);
+  st.mc = mref;
+  return moved;
+}
+
+}  // namespace
+
+template <int NW, bool CAUSAL, bool PAIR>
+__device__ __forceinline__ void fwd_fp8_body(const FwdParams& p, float v_descale) {
+  constexpr int BR = NW * 32;
+  __shared__ __attribute__((aligned(1024))) char k_lds0[kTile8];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[kTile8];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[kTile8];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[kTile8];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m32 = lane & 31, hh = lane >> 5;
+
+  const int item = xcd_remap(blockIdx.x, p.total, p.group * p.n_items);
+  const int it = item % p.n_items;
+  int rest = item / p.n_items;
+  const int hg = rest % p.group;
+  rest /= p.group;
+  const int kvh = rest % p.hkv;
+  const int b = rest / p.hkv;
+  const int h = kvh * p.group + hg;
+
+  int q_start, Lq, k_start, Lk;
+  if (p.cu_q) {
+    q_start = p.cu_q[b];
+    Lq = p.cu_q[b + 1] - q_start;
+    k_start = p.cu_k[b];
+    Lk = p.cu_k[b + 1] - k_start;
+  } else {
+    q_start = b * p.seqlen_q;
+    Lq = p.seqlen_q;
+    k_start = b * p.seqlen_k;
+    Lk = p.seqlen_k;
+  }
+  const uint8_t* q8 = reinterpret_cast<const uint8_t*>(p.q);
+  const uint8_t* k8 = reinterpret_cast<const uint8_t*>(p.k);
+  const uint8_t* v8 = reinterpret_cast<const uint8_t*>(p.v);
+  const int q_stride = p.hq * kD8;   // bytes per token row
+  const int kv_stride = p.hkv * kD8;
+  const uint8_t* kbase = k8 + (size_t)k_start * kv_stride + (size_t)kvh * kD8;
+  const uint8_t* vbase = v8 + (size_t)k_start * kv_stride + (size_t)kvh * kD8;
+
+  auto run_tile = [&](const int qt) __attribute__((always_inline)) {
+    const int q0 = qt * BR;
+    const int delta = Lk - Lq;  // bottom-right causal offset
+    int n_kt = (Lk + kBC8 - 1) / kBC8;
+    if (CAUSAL) {
+      const int last_key = min(Lk - 1, q0 + BR - 1 + delta);
+      n_kt = last_key < 0 ? 0 : min(n_kt, last_key / kBC8 + 1);
+    }
+    const int qw0 = q0 + wave * 32;
+    const bool wave_active = qw0 < Lq;
+    const int wave_last_key = CAUSAL ? min(Lk - 1, qw0 + 31 + delta) : Lk - 1;
+    const int wn =
+        (wave_active && wave_last_key >= 0) ? min(n_kt, wave_last_key / kBC8 + 1) : 0;
+
+    Dma8<NW, false> dk;
+    Dma8<NW, true> dv;
+    dk.init(kv_stride, wave, lane);
+    dv.init(kv_stride, wave, lane);
+    Rd8 rd;
+    rd.init(lane);
+    if (n_kt > 0) dk.issue(kbase, kv_stride, 0, Lk - 1, k_lds0, wave, lane);
+
+    State8 st;
+    st.mc = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) st.o[dt][v] = 0.f;
+    const int qi = qw0 + m32;
+    {
+      const uint8_t* qp = q8 + (size_t)(q_start + qi) * q_stride + (size_t)h * kD8 + 32 * hh;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+        if (qi < Lq) {
+          lo = *reinterpret_cast<const u32x4*>(qp + 64 * s);
+          hi = *reinterpret_cast<const u32x4*>(qp + 64 * s + 16);
+        }
+        const i32x8 r = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        st.qf[s] = r;
+      }
+    }
+    // last admissible key of this lane's row minus 4 hh (the lane's key
+    // offset inside a 32-key sub-tile); tile j masks against lim - 64 j
+    const int row_lim = (CAUSAL ? min(Lk - 1, qi + delta) : Lk - 1) - 4 * hh;
+    auto edge_tile = [&](int j) {
+      const int k0 = j * kBC8;
+      return (k0 + kBC8 > Lk) || (CAUSAL && k0 + kBC8 - 1 > qw0 + delta);
+    };
+
+    i32x8 pb;
+    float alpha = 1.f;
+    bool moved = false;
+#pragma clang loop unroll(disable)
+    for (int j = 0; j <= n_kt; ++j) {
+      // K_j and V_{j-1} have landed; K_{j+1} and V_j stream into the stages
+      // that K_{j-1} and V_{j-2} used
+      wait_dma();
+      __syncthreads();
+      if (j + 1 < n_kt)
+        dk.issue(kbase, kv_stride, (j + 1) * kBC8, Lk - 1, (j & 1) ? k_lds0 : k_lds1, wave, lane);
+      if (j < n_kt) dv.issue(vbase, kv_stride, j * kBC8, Lk - 1, (j & 1) ? v_lds1 : v_lds0, wave, lane);
+      const char* k_cur = (j & 1) ? k_lds1 : k_lds0;
+      const char* v_prev = (j & 1) ? v_lds0 : v_lds1;
+      if (j >= 1 && j <= wn) {
+        if (__any(moved)) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) st.o[dt][v] *= alpha;
+        }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) st.o[dt] = mfma_fp8(rd.v(v_prev, dt), pb, st.o[dt]);
+      }
+      if (j < wn) {
+        f32x16 s[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          s[kt] = mfma_fp8(rd.k(k_cur, kt, 0), st.qf[0], f32x16{});
+          s[kt] = mfma_fp8(rd.k(k_cur, kt, 1), st.qf[1], s[kt]);
+        }
+        if (edge_tile(j)) {
+          const int lim = row_lim - j * kBC8;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              if ((v & 3) + 8 * (v >> 2) + 32 * kt > lim) s[kt][v] = -INFINITY;
+        }
+        moved = softmax8(st, s, pb, alpha, p.c);
+      }
+    }
+
+    // ---- epilogue: O dv / l, LSE = ln 2 (r + log2 l) ----
+    const float lt = halfwave_sum(st.l);
+    const float inv = lt > 0.f ? v_descale / lt : 0.f;
+    const float lse = lt > 0.f ? (st.mc + __log2f(lt)) * kLn2 : -INFINITY;
+    if (qi < Lq) {
+      const size_t orow = (size_t)(q_start + qi) * p.hq + h;
+      if (p.o_f32) {
+        float* op = reinterpret_cast<float*>(p.o) + orow * kD8 + 4 * hh;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 w = {st.o[dt][4 * g] * inv, st.o[dt][4 * g + 1] * inv,
+                             st.o[dt][4 * g + 2] * inv, st.o[dt][4 * g + 3] * inv};
+            *reinterpret_cast<f32x4*>(op + dt * 32 + 8 * g) = w;
+          }
+      } else {
+        uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + orow * kD8 + 4 * hh;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const u32x2 w = {pack_bf16x2(st.o[dt][4 * g] * inv, st.o[dt][4 * g + 1] * inv),
+                             pack_bf16x2(st.o[dt][4 * g + 2] * inv, st.o[dt][4 * g + 3] * inv)};
+            *reinterpret_cast<u32x2*>(op + dt * 32 + 8 * g) = w;
+          }
+      }
+      if (hh == 0) p.lse[orow] = lse;
+    }
+  };  // run_tile
+
+  if constexpr (PAIR) {
+    // causal: tile n-1-i (heaviest) with tile i, per sequence
+    const int first = (Lq + BR - 1) / BR - 1 - it;
+    if (first < it) return;  // past the middle of a shorter sequence (uniform)
+    run_tile(first);
+    if (it < first) {
+      __syncthreads();  // every wave is done with the first tile's LDS stages
+      run_tile(it);
+    }
+  } else {
+    if (it * BR < Lq) run_tile(it);
+  }
+}
+
+template <int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_fp8_kernel(const FwdParams p, float v_descale) {
+  fwd_fp8_body<NW, CAUSAL, CAUSAL>(p, v_descale);
+}
+
+template __global__ void fwd_fp8_kernel<4, false>(const FwdParams, float);
+template __global__ void fwd_fp8_kernel<4, true>(const FwdParams, float);
+template __global__ void fwd_fp8_kernel<8, false>(const FwdParams, float);
+template __global__ void fwd_fp8_kernel<8, true>(const FwdParams, float);
+
+hipError_t launch_fwd_fp8(const FwdParams& p, bool causal, float v_descale, hipStream_t stream) {
+  auto go = [&](auto kern, int threads) {
+    hipLaunchKernelGGL(kern, dim3(p.total), dim3(threads), 0, stream, p, v_descale);
+    return hipGetLastError();
+  };
+  if (p.waves == 8)
+    return causal ? go(fwd_fp8_kernel<8, true>, 512) : go(fwd_fp8_kernel<8, false>, 512);
+  return causal ? go(fwd_fp8_kernel<4, true>, 256) : go(fwd_fp8_kernel<4, false>, 256);
+}
+
+}  // namespace fa

@@ -119,6 +119,8 @@ int fwd_waves(int head_dim, bool varlen, int seqlen_q);
 int fwd_block_rows(int waves);
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream);
+// FP8 forward (head dim 128): p.c = scale * q_descale * k_descale * log2(e).
+hipError_t launch_fwd_fp8(const FwdParams& p, bool causal, float v_descale, hipStream_t stream);
 hipError_t launch_fwd_local(const FwdParams& p, int head_dim, bool causal, int win_left,
                             int win_right, hipStream_t stream);
 hipError_t launch_fwd_xf(const FwdParams& p, int head_dim, bool causal, int win_left,

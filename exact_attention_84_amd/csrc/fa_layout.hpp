@@ -65,4 +65,65 @@ FA_HD constexpr int v_read_offset(int lane, int dt, int sec) {
          8 * (k & 1);
 }
 
+// ---------------------------------------------------------------------------
+// FP8 (E4M3) tiles, head dim 128: row r (one key) holds 128 one-byte values,
+// 8 chunks of 16 bytes, two rows per 256-byte bank cycle.
+//
+// Both products use v_mfma_scale_f32_32x32x64_f8f6f4, whose A and B operands
+// give every lane 32 bytes (byte s = slot s).  The two operands pair their
+// slots identically, so any assignment of the contraction index to (half-wave
+// hh, slot s) that both operands follow gives the product:
+//   * S^T = K Q^T: head-dim index 64 st + 32 hh + s for k-step st, i.e. 32
+//     consecutive bytes of the key row (A) and of the query row (B);
+//   * O^T = V^T P^T: key pv8_key(hh, s) of the 64-key tile, the key that
+//     element s = 16 kt + v of the lane's S^T accumulators holds, so P goes
+//     from the accumulators into the B operand in order.
+// ---------------------------------------------------------------------------
+FA_HD constexpr int pv8_key(int hh, int s) {
+  return ((s & 15) & 3) + 8 * ((s & 15) >> 2) + 4 * hh + 32 * (s >> 4);
+}
+
+// K tile swizzle: the 16 rows one 16-byte operand read serves per clock
+// (rows r0..r0+15, one logical chunk) land on 16 distinct 16-byte bank groups.
+FA_HD constexpr int k8_swizzle(int r) { return (r >> 1) & 7; }
+// V tile swizzle: the 32 lanes one transposing read serves per clock (8 key
+// rows {0..3, 8..11} + 4 hh + 16 q, two logical chunks, two 8-byte halves)
+// land on 16 distinct bank groups, two halves each.
+FA_HD constexpr int v8_swizzle(int r) { return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2); }
+
+FA_HD constexpr int k8_offset(int row, int chunk) {
+  return row * 128 + ((chunk ^ k8_swizzle(row)) << 4);
+}
+FA_HD constexpr int v8_offset(int row, int chunk) {
+  return row * 128 + ((chunk ^ v8_swizzle(row)) << 4);
+}
+
+// DMA of an FP8 tile: wave instruction i writes bytes [1024 i, +1024), lane l
+// the 16 bytes of row 8 i + l / 8 at physical chunk l % 8, which hold logical
+// chunk dma8_chunk(...) of that row.
+FA_HD constexpr int dma8_row(int inst, int lane) { return 8 * inst + lane / 8; }
+FA_HD constexpr int dma8_chunk(int inst, int lane, bool v_tile) {
+  return (lane % 8) ^ (v_tile ? v8_swizzle(dma8_row(inst, lane)) : k8_swizzle(dma8_row(inst, lane)));
+}
+
+// A operand of S^T = K Q^T, k-step st, 16-byte half u of the lane's 32 bytes:
+// key row lane % 32 (+32 kt adds 4096 bytes: same swizzle), logical chunk
+// 4 st + 2 hh + u.
+FA_HD constexpr int k8_read_offset(int lane, int st, int u) {
+  return k8_offset(lane & 31, 4 * st + 2 * (lane >> 5) + u);
+}
+
+// A operand of O^T = V^T P^T for head-dim rows 32 dt.. with four transposing
+// reads (ds_read_b64_tr_b8), read q giving slots 8 q .. 8 q + 7.  Within each
+// group of 16 lanes that read hands result lane i, byte j, the byte i % 8 of
+// the 8 bytes source lane 2 j + (i / 8) % 2 addressed.  So source lane s of
+// group g (j = (s % 16) / 2, c = s % 2, hh = g / 2) addresses key row
+// pv8_key(hh, 8 q + j) and head-dim columns 32 dt + 16 (g % 2) + 8 c .. +7:
+// logical chunk 2 dt + g % 2, half c.  Read q adds 16 q rows (2048 q bytes;
+// the swizzle does not see row bits 4 and 5).
+FA_HD constexpr int v8_read_offset(int lane, int dt) {
+  const int g = (lane & 63) >> 4, j = (lane & 15) >> 1, c = lane & 1, hh = g >> 1;
+  return v8_offset(pv8_key(hh, j), 2 * dt + (g & 1)) + 8 * c;
+}
+
 }  // namespace fa

@@ -124,6 +124,35 @@ fa_status fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float
                      fa_dtype o_dtype, void* stream);
 
 /*
+ * fa_fwd_fp8 -- the forward on FP8 inputs, both products on the FP8 matrix
+ * cores (the first page's FlashAttention 3 notes, "推理优化 | FlashAttention
+ * 1-4 详解", section FlashAttention 3 的硬件特性利用: FP8 matrix products in
+ * the forward).  q, k, v hold OCP E4M3 codes (one byte each: 1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits, S.1111.111 = NaN, largest
+ * finite 448), in fa_fwd's layouts; the real tensors are q_descale * q,
+ * k_descale * k and v_descale * v.  Computes fa_fwd's O and lse of those real
+ * tensors (same batching, varlen, causal and GQA rules), with these
+ * differences:
+ *   head_dim            : 128 only (FA_ERR_HEADDIM otherwise);
+ *   q/k/v_descale       : finite and > 0 (FA_ERR_ARG otherwise);
+ *   precision           : the scores are exact products of E4M3 values summed
+ *                         by the FP8 matrix core (whose internal accumulation
+ *                         is not exact fp32: measured errors reach about
+ *                         2^-12 of the largest product in a 64-term sum);
+ *                         the probabilities exp(s - r) are rounded to E4M3
+ *                         before the product with V (r within 8 log2 units of
+ *                         the row maximum), the row sum uses the unrounded
+ *                         ones; O is scaled by v_descale in fp32.
+ * Inputs containing NaN codes give NaN outputs.
+ */
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k,
+                     int head_dim, float scale, float q_descale, float k_descale,
+                     float v_descale, int causal, const int32_t* cu_seqlens_q,
+                     const int32_t* cu_seqlens_k, int max_seqlen_q, int max_seqlen_k,
+                     fa_dtype o_dtype, void* stream);
+
+/*
  * fa_decode_workspace_size -- bytes of float32 scratch that
  * fa_fwd_decode_splitkv needs for these sizes (partial O and LSE of every
  * key chunk).  chunk = 0 selects the built-in chunk size.  Returns 0 for

@@ -121,6 +121,34 @@ def test_fwd_ext_empty_inputs_are_noops(lib):
     assert fwd_ext(lib, nq=0, q=None, o=None, lse=None, alibi=FAKE, astride=8) == OK
 
 
+def fwd_fp8(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, batch=2, hq=8, hkv=2, nq=16, nk=16, d=128,
+             scale=0.088, dq=0.5, dk=0.25, dv=2.0, causal=1, cuq=None, cuk=None, mq=0, mk=0,
+             odt=0, stream=None)
+    a.update(kw)
+    return lib.fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["batch"], a["hq"],
+                          a["hkv"], a["nq"], a["nk"], a["d"], a["scale"], a["dq"], a["dk"],
+                          a["dv"], a["causal"], a["cuq"], a["cuk"], a["mq"], a["mk"], a["odt"],
+                          a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=64), HEADDIM), (dict(d=96), HEADDIM),
+    (dict(dq=0.0), ARG), (dict(dk=-1.0), ARG), (dict(dv=float("nan")), ARG),
+    (dict(dq=float("inf")), ARG), (dict(dq=1e30, dk=1e30), ARG),
+    (dict(q=None), NULL), (dict(v=None), NULL), (dict(hkv=3), GQA), (dict(scale=0.0), ARG),
+    (dict(causal=2), ARG), (dict(odt=7), DTYPE), (dict(nq=-1), SHAPE),
+])
+def test_fwd_fp8_rejects_before_launch(lib, kw, status):
+    assert fwd_fp8(lib, **kw) == status
+    assert lib.fa_last_error().decode()
+
+
+def test_fwd_fp8_empty_inputs_are_noops(lib):
+    assert fwd_fp8(lib, batch=0) == OK
+    assert fwd_fp8(lib, nq=0, q=None, o=None, lse=None) == OK
+
+
 def dec(lib, **kw):
     a = dict(q=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, o=FAKE, lse=FAKE, batch=4, hq=32, hkv=8,
              ncache=4096, d=128, scale=0.088, chunk=0, ws=FAKE, wsb=1 << 40, odt=0, stream=None)

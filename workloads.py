@@ -184,6 +184,23 @@ def make_fixed_fp8(batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim, *, se
     return q, k, v, descales
 
 
+def make_varlen_fp8(lengths_q, lengths_k, heads_q, heads_kv, head_dim, *, seed=0, wid=0):
+    """Packed E4M3 codes q8 [sum Lq, Hq, d], k8/v8 [sum Lk, Hkv, d], int32
+    cu_seqlens and the per-tensor descales (q, k, v)."""
+    lengths_q = np.asarray(lengths_q, np.int32)
+    lengths_k = np.asarray(lengths_k, np.int32)
+    cu_q, cu_k = prefix_sums(lengths_q), prefix_sums(lengths_k)
+    q = np.empty((int(cu_q[-1]), heads_q, head_dim), np.uint8)
+    k = np.empty((int(cu_k[-1]), heads_kv, head_dim), np.uint8)
+    v = np.empty((int(cu_k[-1]), heads_kv, head_dim), np.uint8)
+    for s in range(len(lengths_q)):
+        q[cu_q[s]:cu_q[s + 1]] = normal_fp8(seed, wid, T_Q, (lengths_q[s], heads_q, head_dim), s)
+        k[cu_k[s]:cu_k[s + 1]] = normal_fp8(seed, wid, T_K, (lengths_k[s], heads_kv, head_dim), s)
+        v[cu_k[s]:cu_k[s + 1]] = normal_fp8(seed, wid, T_V, (lengths_k[s], heads_kv, head_dim), s)
+    descales = tuple(1.0 / FP8_MULT[t] for t in (T_Q, T_K, T_V))
+    return q, k, v, cu_q, cu_k, descales
+
+
 BF16_NAN = np.uint16(0x7FC0)
 
 
