@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 METRIC = "attention fwd TFLOP/s (4·B·H·Nq·Nk·d, causal halved) and % of bf16 MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -310,6 +311,33 @@ def window_workload(fa, w, steps, warmup):
     return res
 
 
+def fp8_workload(fa, w, steps, warmup):
+    """The headline workload's shape with E4M3 inputs (N(0,1) draws scaled per
+    tensor and cast; descales 1/32, 1/16, 1/64) through the FP8 forward,
+    non-causal and causal.  Algorithmic flops as the bf16 forward's; the
+    share is of the dense FP8 peak."""
+    import torch
+    q8, k8, v8, ds = W.make_fixed_fp8(w.batch, w.heads_q, w.heads_kv, w.seqlen_q, w.seqlen_k,
+                                      w.head_dim, seed=0, wid=w.wid)
+    q, k, v = (torch.from_numpy(x).cuda() for x in (q8, k8, v8))
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+    res = {}
+    for causal in (False, True):
+        fl = W.flops(w, causal=causal)
+        ms = time_calls(lambda: fa.attention_fp8(q, k, v, q_descale=ds[0], k_descale=ds[1],
+                                                 v_descale=ds[2], causal=causal, scale=w.scale,
+                                                 out=o, lse=lse),
+                        steps, warmup)
+        tf = fl / (ms * 1e-3) / 1e12
+        res["causal" if causal else "noncausal"] = {
+            "ms": round(ms, 4), "tflops": round(tf, 1),
+            "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4), "gflop": round(fl / 1e9, 1)}
+        log("fp8 forward", w.name, "causal" if causal else "non-causal",
+            res["causal" if causal else "noncausal"])
+    return res
+
+
 def backward_workload(fa, w, steps, warmup):
     """The attention backward (preprocess, dK/dV and dQ kernels) on the
     headline workload, non-causal and causal, from the forward's own O and
@@ -565,6 +593,9 @@ def main():
             kvcache_workload(fa, W.WORKLOADS[5], max(5, a.steps // 5), max(3, a.warmup // 5))
         res["other_workloads"]["gqa_causal_b1_h32kv8_n8192_d128_sliding_window"] = \
             window_workload(fa, W.WORKLOADS[3], max(5, a.steps // 5), max(3, a.warmup // 5))
+        res["fp8_forward"] = {"workload": w.name, "dtype": "e4m3 inputs, fp32 accumulation",
+                              "o_dtype": "bf16",
+                              **fp8_workload(fa, w, max(5, a.steps // 5), max(3, a.warmup // 5))}
         res["backward"] = {"workload": w.name, "grad_dtype": "bf16",
                            **backward_workload(fa, w, max(5, a.steps // 5),
                                                max(3, a.warmup // 5))}

@@ -40,6 +40,19 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// One direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l writes lds_dst + 16 l.  Issued as inline assembly, so that the
+// compiler does not make every later LDS read wait for all such loads (it
+// cannot tell the stages apart); the kernel waits for exactly the loads a
+// step needs (wait_tiles_upto) and then meets at a barrier.  M0 holds the
+// wave's LDS destination; the load reads M0 one wait state after it is set.
+__device__ __forceinline__ void dma16(const void* g, char* lds_dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds_dst)));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(m0) : "memory", "m0");
+}
+
 // Direct global->LDS fill of one 64-row FP8 tile: 8 wave instructions of
 // 64 x 16 bytes, NW waves issuing 8 / NW each.  Rows past klast are read from
 // row klast (their scores are masked, so they only meet zero probabilities).
@@ -62,8 +75,7 @@ struct Dma8 {
     if (k0 + kBC8 - 1 <= klast) {
 #pragma unroll
       for (int n = 0; n < PER_WAVE; ++n)
-        __builtin_amdgcn_global_load_lds(tile + off[n], (lds_void*)(lds + (wave + n * NW) * 1024),
-                                         16, 0, 0);
+        dma16(tile + off[n], lds + (wave + n * NW) * 1024);
     } else {
 #pragma unroll
       for (int n = 0; n < PER_WAVE; ++n) {
@@ -71,7 +83,7 @@ struct Dma8 {
         const int src = min(k0 + dma8_row(inst, lane), klast);
         const uint8_t* g =
             base + (size_t)src * row_stride + (dma8_chunk(inst, lane, V_TILE) << 4);
-        __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds + inst * 1024), 16, 0, 0);
+        dma16(g, lds + inst * 1024);
       }
     }
   }
@@ -112,6 +124,18 @@ struct Rd8 {
     return r;
   }
 };
+
+// Waits until at most `tiles` tile loads of this wave (PER instructions
+// each) are still in flight: the loads of a step complete in issue order.
+template <int PER>
+__device__ __forceinline__ void wait_tiles_upto(int tiles) {
+  if (tiles <= 0)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (tiles == 1)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory");
+}
 
 struct State8 {
   i32x8 qf[2];     // Q^T, B operand of S^T = K Q^T, per k-step
@@ -155,15 +179,95 @@ __device__ __forceinline__ bool softmax8(State8& st, f32x16 (&s)[2], i32x8& pb, 
   return moved;
 }
 
+// Sets to -inf every score of a 64-key tile past the lane's limit: element v
+// of sub-tile kt holds key (v & 3) + 8 (v >> 2) + 32 kt + 4 hh of the tile,
+// and lim already has 4 hh taken off.
+__device__ __forceinline__ void mask8(f32x16 (&s)[2], int lim) {
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if ((v & 3) + 8 * (v >> 2) + 32 * kt > lim) s[kt][v] = -INFINITY;
+}
+
+// S^T sub-tiles of a 64-key tile: two k-steps of 64 head-dim values each.
+__device__ __forceinline__ void scores8(f32x16 (&s)[2], const char* __restrict__ k_cur,
+                                        const Rd8& rd, const State8& st) {
+  const i32x8 a0 = rd.k(k_cur, 0, 0), a1 = rd.k(k_cur, 1, 0);
+  const i32x8 b0 = rd.k(k_cur, 0, 1), b1 = rd.k(k_cur, 1, 1);
+  s[0] = mfma_fp8(a0, st.qf[0], f32x16{});
+  s[1] = mfma_fp8(a1, st.qf[0], f32x16{});
+  s[0] = mfma_fp8(b0, st.qf[1], s[0]);
+  s[1] = mfma_fp8(b1, st.qf[1], s[1]);
+}
+
+// One steady step: S_j = K_j Q^T, then the four P_{j-1} V_{j-1} MFMAs, each
+// followed by a slice of the softmax of S_j (sched_barrier fences keep that
+// order), so that the ALUs work while the matrix core runs: the row maximum
+// and new reference after the first, the probabilities of 12, 12 and 8 keys
+// after the others.  pout receives P_j; returns whether the row moved its
+// reference (alpha then holds the rescale factor, applied before P_j V_j).
+__device__ __forceinline__ bool steady8(State8& st, const char* __restrict__ k_cur,
+                                        const char* __restrict__ v_prev, const Rd8& rd,
+                                        const i32x8& pin, i32x8& pout, float& alpha, float c,
+                                        bool masked, int lim) {
+  f32x16 s[2];
+  scores8(s, k_cur, rd, st);
+  if (masked) mask8(s, lim);
+  float mref = 0.f, msub = 0.f, rs = 0.f;
+  i32x8 va = rd.v(v_prev, 0);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const i32x8 vcur = va;
+    if (dt < 3) va = rd.v(v_prev, dt + 1);
+    st.o[dt] = mfma_fp8(vcur, pin, st.o[dt]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (dt == 0) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt][v]);
+      const float mx_c = halfwave_max(mx) * c;
+      mref = (mx_c > st.mc + kRescaleTau) ? mx_c : st.mc;
+      msub = (mref == -INFINITY) ? 0.f : mref;
+      alpha = fast_exp2(st.mc - msub);
+    } else {
+      const int w0 = dt == 1 ? 0 : (dt == 2 ? 3 : 6);
+      const int w1 = dt == 1 ? 3 : (dt == 2 ? 6 : 8);
+#pragma unroll
+      for (int w = w0; w < w1; ++w) {
+        float pr[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int idx = 4 * w + e;
+          pr[e] = fast_exp2(fmaf(s[idx >> 4][idx & 15], c, -msub));
+          rs += pr[e];
+        }
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
+        x = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], x, true);
+        pout[w] = x;
+        // keep the conversion in this slice
+        asm volatile("" ::"v"(x));
+      }
+      asm volatile("" : "+v"(rs));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  st.l = fmaf(alpha, st.l, rs);
+  const bool moved = mref != st.mc;
+  st.mc = mref;
+  return moved;
+}
+
 }  // namespace
 
 template <int NW, bool CAUSAL, bool PAIR>
 __device__ __forceinline__ void fwd_fp8_body(const FwdParams& p, float v_descale) {
   constexpr int BR = NW * 32;
-  __shared__ __attribute__((aligned(1024))) char k_lds0[kTile8];
-  __shared__ __attribute__((aligned(1024))) char k_lds1[kTile8];
-  __shared__ __attribute__((aligned(1024))) char v_lds0[kTile8];
-  __shared__ __attribute__((aligned(1024))) char v_lds1[kTile8];
+  // Three stages of K and V: tiles j+1 and j+2 stream in while tile j is used.
+  __shared__ __attribute__((aligned(1024))) char k_lds[3 * kTile8];
+  __shared__ __attribute__((aligned(1024))) char v_lds[3 * kTile8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -219,7 +323,11 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdParams& p, float v_descale
     dv.init(kv_stride, wave, lane);
     Rd8 rd;
     rd.init(lane);
-    if (n_kt > 0) dk.issue(kbase, kv_stride, 0, Lk - 1, k_lds0, wave, lane);
+    // K_0, then K_1 and V_0 (step j waits for K_j and V_{j-1}, issued a step
+    // before the loads it may leave in flight)
+    if (n_kt > 0) dk.issue(kbase, kv_stride, 0, Lk - 1, k_lds, wave, lane);
+    if (n_kt > 1) dk.issue(kbase, kv_stride, kBC8, Lk - 1, k_lds + kTile8, wave, lane);
+    if (n_kt > 0) dv.issue(vbase, kv_stride, 0, Lk - 1, v_lds, wave, lane);
 
     State8 st;
     st.mc = -INFINITY;
@@ -242,6 +350,10 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdParams& p, float v_descale
                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         st.qf[s] = r;
       }
+      // Q has landed before the key loop: otherwise the compiler's wait for
+      // it sits at its first use inside the loop and waits for every tile
+      // load in flight on each step
+      asm volatile("" ::"v"(st.qf[0]), "v"(st.qf[1]));
     }
     // last admissible key of this lane's row minus 4 hh (the lane's key
     // offset inside a 32-key sub-tile); tile j masks against lim - 64 j
@@ -251,48 +363,80 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdParams& p, float v_descale
       return (k0 + kBC8 > Lk) || (CAUSAL && k0 + kBC8 - 1 > qw0 + delta);
     };
 
-    i32x8 pb;
+    i32x8 p_a, p_b;
     float alpha = 1.f;
     bool moved = false;
-#pragma clang loop unroll(disable)
-    for (int j = 0; j <= n_kt; ++j) {
-      // K_j and V_{j-1} have landed; K_{j+1} and V_j stream into the stages
-      // that K_{j-1} and V_{j-2} used
-      wait_dma();
+    constexpr int PER = Dma8<NW, false>::PER_WAVE;
+    int s0 = 0;  // stage of K_j and V_j: j mod 3
+    // Step j: K_j and V_{j-1} have landed once at most the previous step's
+    // loads (K_{j+1}, V_j) are in flight; then K_{j+2} and V_{j+1} stream
+    // into the stages that K_{j-1} and V_{j-2} used.  Sets the stages of K_j
+    // and V_{j-1}.
+    const char* k_cur;
+    const char* v_prev;
+    auto stage = [&](int j) {
+      const int s1 = s0 == 2 ? 0 : s0 + 1;  // (j + 1) mod 3
+      const int s2 = s1 == 2 ? 0 : s1 + 1;  // (j + 2) mod 3 = (j - 1) mod 3
+      wait_tiles_upto<PER>((j + 1 < n_kt ? 1 : 0) + (j < n_kt ? 1 : 0));
       __syncthreads();
+      if (j + 2 < n_kt)
+        dk.issue(kbase, kv_stride, (j + 2) * kBC8, Lk - 1, k_lds + s2 * kTile8, wave, lane);
       if (j + 1 < n_kt)
-        dk.issue(kbase, kv_stride, (j + 1) * kBC8, Lk - 1, (j & 1) ? k_lds0 : k_lds1, wave, lane);
-      if (j < n_kt) dv.issue(vbase, kv_stride, j * kBC8, Lk - 1, (j & 1) ? v_lds1 : v_lds0, wave, lane);
-      const char* k_cur = (j & 1) ? k_lds1 : k_lds0;
-      const char* v_prev = (j & 1) ? v_lds0 : v_lds1;
+        dv.issue(vbase, kv_stride, (j + 1) * kBC8, Lk - 1, v_lds + s1 * kTile8, wave, lane);
+      k_cur = k_lds + s0 * kTile8;
+      v_prev = v_lds + s2 * kTile8;
+      s0 = s1;
+    };
+    // the O rescale of step j-1's softmax lands between P_{j-2} V and P_{j-1} V
+    auto rescale = [&]() {
+      if (__any(moved)) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) st.o[dt][v] *= alpha;
+      }
+    };
+    // One step done phase by phase: the first tile (no P V yet), the final
+    // P V, and steps where this wave has nothing left.  P_{j-1} is in p_a.
+    auto general_step = [&](int j) {
+      stage(j);
       if (j >= 1 && j <= wn) {
-        if (__any(moved)) {
+        rescale();
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) st.o[dt][v] *= alpha;
-        }
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) st.o[dt] = mfma_fp8(rd.v(v_prev, dt), pb, st.o[dt]);
+        for (int dt = 0; dt < 4; ++dt) st.o[dt] = mfma_fp8(rd.v(v_prev, dt), p_a, st.o[dt]);
       }
       if (j < wn) {
         f32x16 s[2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          s[kt] = mfma_fp8(rd.k(k_cur, kt, 0), st.qf[0], f32x16{});
-          s[kt] = mfma_fp8(rd.k(k_cur, kt, 1), st.qf[1], s[kt]);
+        scores8(s, k_cur, rd, st);
+        if (edge_tile(j)) mask8(s, row_lim - j * kBC8);
+        moved = softmax8(st, s, p_a, alpha, p.c);
+      }
+    };
+    auto steady = [&](int j, const i32x8& pin, i32x8& pout) {
+      stage(j);
+      rescale();
+      moved = steady8(st, k_cur, v_prev, rd, pin, pout, alpha, p.c, edge_tile(j),
+                      row_lim - j * kBC8);
+    };
+    int j = 0;
+    if (wn > 1) {
+      general_step(0);
+      j = 1;
+      // unrolled by two so that the probability registers swap statically
+#pragma clang loop unroll(disable)
+      while (j < wn) {
+        steady(j, p_a, p_b);
+        ++j;
+        if (j >= wn) {
+          p_a = p_b;  // the generic step expects P_{j-1} in p_a
+          break;
         }
-        if (edge_tile(j)) {
-          const int lim = row_lim - j * kBC8;
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-              if ((v & 3) + 8 * (v >> 2) + 32 * kt > lim) s[kt][v] = -INFINITY;
-        }
-        moved = softmax8(st, s, pb, alpha, p.c);
+        steady(j, p_b, p_a);
+        ++j;
       }
     }
+#pragma clang loop unroll(disable)
+    for (; j <= n_kt; ++j) general_step(j);
 
     // ---- epilogue: O dv / l, LSE = ln 2 (r + log2 l) ----
     const float lt = halfwave_sum(st.l);
