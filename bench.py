@@ -94,6 +94,7 @@ TRAFFIC_KERNELS = {
     "decode_kernel<128>": ("decode_d128", "fa_decode.hip"),
     "bwd_dkdv_kernel<128, false>": ("bwd_dkdv_noncausal_d128", "fa_bwd.hip"),
     "bwd_dq_kernel<128, 4, false>": ("bwd_dq_noncausal_d128", "fa_bwd.hip"),
+    "fwd_fp8_kernel<8, false>": ("fwd_fp8_noncausal_d128", "fa_fwd_fp8.hip"),
 }
 
 
@@ -333,6 +334,8 @@ def fp8_workload(fa, w, steps, warmup):
         res["causal" if causal else "noncausal"] = {
             "ms": round(ms, 4), "tflops": round(tf, 1),
             "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4), "gflop": round(fl / 1e9, 1)}
+        if not causal:
+            res["noncausal"]["traffic"] = measured_traffic("fwd_fp8_noncausal_d128")
         log("fp8 forward", w.name, "causal" if causal else "non-causal",
             res["causal" if causal else "noncausal"])
     return res
@@ -406,7 +409,7 @@ def decode_inputs(fa, w):
 def probe(fa, w, steps, warmup):
     """Launches for rocprofv3 counter runs: the headline workload's non-causal
     and causal forward, the split-KV decode workload, the headline workload's
-    non-causal backward (bf16 gradients), then a 1 GiB
+    non-causal backward (bf16 gradients), its non-causal FP8 forward, then a 1 GiB
     device-to-device copy (a kernel that reads and writes exactly 1 GiB each,
     to scale the byte counters)."""
     import torch
@@ -432,12 +435,21 @@ def probe(fa, w, steps, warmup):
         fa.attention_backward(q, k, v, o, lse, do, causal=False, scale=w.scale, workspace=ws,
                               grad_dtype=torch.bfloat16)
     del q, k, v, do, o, lse, ws
+    q8, k8, v8, ds = W.make_fixed_fp8(w.batch, w.heads_q, w.heads_kv, w.seqlen_q, w.seqlen_k,
+                                      w.head_dim, seed=0, wid=w.wid)
+    q, k, v = (torch.from_numpy(x).cuda() for x in (q8, k8, v8))
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+    for _ in range(warmup + steps):
+        fa.attention_fp8(q, k, v, q_descale=ds[0], k_descale=ds[1], v_descale=ds[2],
+                         causal=False, scale=w.scale, out=o, lse=lse)
+    del q, k, v, o, lse
     a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
     for _ in range(steps):
         b.copy_(a)
     torch.cuda.synchronize()
-    log(f"probe: {warmup + steps} non-causal, causal, decode and backward launches, "
+    log(f"probe: {warmup + steps} non-causal, causal, decode, backward and FP8 launches, "
         f"{steps} copies of {a.numel() * 4} bytes")
 
 

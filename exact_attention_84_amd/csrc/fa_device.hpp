@@ -125,6 +125,13 @@ struct WaveState {
 #endif
 constexpr float kRescaleTau = FA_RESCALE_TAU;
 
+// Largest accepted sum of one lane's probabilities of a tile formed against
+// the unchanged reference (p = 2^(s c - r) <= that sum).  2^kRescaleTau
+// keeps every accepted probability within the bound the row-maximum path
+// gives, so both paths round the same range of values.
+constexpr float kSumCap = 256.0f;
+static_assert(kSumCap <= 448.0f, "accepted probabilities must stay inside the E4M3 range");
+
 // Online-softmax probabilities for NKT score sub-tiles: new reference, the
 // rescale factor alpha, probabilities (fp32 for the row sum, bf16 for the P V
 // product).  Returns whether any row of the wave moved its reference.

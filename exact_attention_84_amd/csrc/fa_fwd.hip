@@ -119,13 +119,22 @@ __device__ __forceinline__ void transform_tile(f32x16 (&s)[NKT][NT], const Score
 // tiles:
 //   s      = Q K_j^T            (D/8 K fragments, NT MFMAs each)
 //   O     += P_{j-1} V_{j-1}    (D/8 V fragments, NT MFMAs each)
-//   softmax of s (tile j) -> pout, alpha
+//   probabilities of s (tile j) -> pout
 // The P V MFMAs do not depend on the new scores, so each of them is followed
-// by a slice of the softmax of s (sched_barrier fences keep that order): the
-// wave keeps issuing ALU instructions while the matrix core works.  Returns
-// whether a row moved its reference (alpha then holds the rescale factors).
-// A tile that crosses the end of the keys or the diagonal is masked first
-// (`masked`, uniform over the wave; limits as in mask_tile).
+// by a slice of the exponentials of s (sched_barrier fences keep that order):
+// the wave keeps issuing ALU instructions while the matrix core works.
+//
+// The probabilities are first formed against each row's current reference r,
+// with no row maximum: p = 2^(s c - r).  Every p of a lane is at most the
+// lane's sum of them, so when no lane's sum exceeds kSumCap (and none is inf
+// or NaN: a row still at r = -inf gives inf or NaN) the reference may stay
+// and the step is done (alpha = 1).  Otherwise the tile's scores, kept
+// unchanged, go through the row-maximum path of softmax_probs, which moves
+// the references.  Either way O and l are
+// accumulated relative to the same r, so the result is the same up to
+// rounding.  Returns whether a row moved its reference (alpha then holds the
+// rescale factors).  A tile that crosses the end of the keys or the diagonal
+// is masked first (`masked`, uniform over the wave; limits as in mask_tile).
 template <int D, int NT, bool LOCAL, bool XF>
 __device__ __forceinline__ bool steady_step(WaveState<D, NT>& st, const char* __restrict__ k_cur,
                                             const char* __restrict__ v_prev, const LdsRead<D>& rd,
@@ -134,6 +143,96 @@ __device__ __forceinline__ bool steady_step(WaveState<D, NT>& st, const char* __
                                             float c, bool masked, const int (&lim)[NT],
                                             const int (&lo)[NT], const ScoreXf& xf,
                                             const int (&rel)[NT]) {
+  constexpr int DT = D / 32;
+  constexpr int SLOTS = D / 8;                  // V fragments per step
+  constexpr int LEAD = 2;                       // P V MFMAs before the first slice
+  constexpr int NE = 32 * NT;                   // probabilities per lane
+  constexpr int EXP_SLOTS = SLOTS - LEAD;
+  static_assert(4 * DT == SLOTS, "slot bookkeeping");
+
+  f32x16 s[2][NT];
+  scores_tile<D, NT, 2>(s, k_cur, rd, st.qf);
+  if constexpr (XF) transform_tile<NT, 2>(s, xf, rel);
+  if (masked) {
+    mask_tile<NT, 2>(s, lim);
+    if constexpr (LOCAL) mask_tile_lo<NT, 2>(s, lo);
+  }
+
+  float rs[NT];
+  uint32_t pk[NT][16];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) rs[t] = 0.f;
+  bf16x8 va = rd.v(v_prev, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) {
+    const int pkt = i / (2 * DT), pu = (i / DT) & 1, pdt = i % DT;
+    const bf16x8 vcur = va;
+    if (i + 1 < SLOTS) {
+      const int n = i + 1;
+      va = rd.v(v_prev, n / (2 * DT), (n / DT) & 1, n % DT);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      st.o[t][pdt] = mfma_32x32x16(vcur, pin[pkt][t][pu], st.o[t][pdt]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i >= LEAD) {
+      // pairs of probabilities g0 .. g1-1 of the lane's NE / 2, spread evenly
+      // over the slots; the scores stay in place for the row-maximum path
+      const int g0 = (i - LEAD) * (NE / 2) / EXP_SLOTS;
+      const int g1 = (i - LEAD + 1) * (NE / 2) / EXP_SLOTS;
+#pragma unroll
+      for (int g = g0; g < g1; ++g) {
+        const int t = g >> 4, e = 2 * (g & 15);
+        const float p0 = fast_exp2(fmaf(s[e >> 4][t][e & 15], c, -st.mc[t]));
+        const float p1 = fast_exp2(fmaf(s[e >> 4][t][(e + 1) & 15], c, -st.mc[t]));
+        rs[t] += p0;
+        rs[t] += p1;
+        pk[t][e >> 1] = pack_bf16x2(p0, p1);
+        // keep the conversion in this slice (it would otherwise sink to its
+        // use in the next step)
+        asm volatile("" ::"v"(pk[t][e >> 1]));
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(rs[t]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  bool ok = true;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) ok = ok && (rs[t] <= kSumCap);
+  if (__builtin_expect(__all(ok), 1)) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const u32x4 w = {pk[t][8 * kt + 4 * u], pk[t][8 * kt + 4 * u + 1],
+                           pk[t][8 * kt + 4 * u + 2], pk[t][8 * kt + 4 * u + 3]};
+          pout[kt][t][u] = __builtin_bit_cast(bf16x8, w);
+        }
+      st.l[t] += rs[t];
+      alpha[t] = 1.f;
+    }
+    return false;
+  }
+  // some row outgrew its reference (or has none yet): the row-maximum path
+  return softmax_probs<D, NT, 2>(st, s, pout, alpha, c);
+}
+
+// The steady step with the row maximum first (the transform instance's):
+// each P V MFMA is followed by a slice of the softmax of s, the row maxima
+// and new references in the first two slices, then the exponentials against
+// the new references.  ALiBi raises the scores of every tile nearer the
+// diagonal, so its references move on most tiles; forming the maxima first
+// costs less there than forming the probabilities twice.  Returns whether a
+// row moved its reference (alpha then holds the rescale factors).
+template <int D, int NT, bool LOCAL, bool XF>
+__device__ __forceinline__ bool steady_step_max_first(
+    WaveState<D, NT>& st, const char* __restrict__ k_cur, const char* __restrict__ v_prev,
+    const LdsRead<D>& rd, const bf16x8 (&pin)[2][NT][2], bf16x8 (&pout)[2][NT][2],
+    float (&alpha)[NT], float c, bool masked, const int (&lim)[NT], const int (&lo)[NT],
+    const ScoreXf& xf, const int (&rel)[NT]) {
   constexpr int DT = D / 32;
   constexpr int SLOTS = D / 8;                  // V fragments per step
   constexpr int LEAD = 2;                       // P V MFMAs before the first slice
@@ -429,8 +528,12 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, int win_left, int w
       lo[t] = row_lo[t] - (kt0 + jj) * BC;
       rel[t] = row_rel[t] - (kt0 + jj) * BC;
     }
-    moved = steady_step<D, NT, LOCAL, XF>(st, k_cur, v_prev, rd, pin, pout, alpha, p.c,
-                                          edge_tile(jj), lim, lo, xf, rel);
+    if constexpr (XF)
+      moved = steady_step_max_first<D, NT, LOCAL, XF>(st, k_cur, v_prev, rd, pin, pout, alpha,
+                                                      p.c, edge_tile(jj), lim, lo, xf, rel);
+    else
+      moved = steady_step<D, NT, LOCAL, XF>(st, k_cur, v_prev, rd, pin, pout, alpha, p.c,
+                                            edge_tile(jj), lim, lo, xf, rel);
   };
   if (wn > 1) {
     general_step(0);  // softmax of S_0 -> p_a

@@ -202,11 +202,15 @@ __device__ __forceinline__ void scores8(f32x16 (&s)[2], const char* __restrict__
 }
 
 // One steady step: S_j = K_j Q^T, then the four P_{j-1} V_{j-1} MFMAs, each
-// followed by a slice of the softmax of S_j (sched_barrier fences keep that
-// order), so that the ALUs work while the matrix core runs: the row maximum
-// and new reference after the first, the probabilities of 12, 12 and 8 keys
-// after the others.  pout receives P_j; returns whether the row moved its
-// reference (alpha then holds the rescale factor, applied before P_j V_j).
+// followed by the exponentials of 8 of the lane's keys (sched_barrier fences
+// keep that order), so that the ALUs work while the matrix core runs.  The
+// probabilities are formed against the row's current reference r with no
+// row maximum; every p is at most the lane's sum of them, so when no sum
+// exceeds kSumCap (and none is inf or NaN) the reference stays and alpha = 1.
+// Otherwise the scores, kept unchanged, go through softmax8, which moves the
+// references.  pout receives P_j; returns
+// whether the row moved its reference (alpha then holds the rescale factor,
+// applied before P_j V_j).
 __device__ __forceinline__ bool steady8(State8& st, const char* __restrict__ k_cur,
                                         const char* __restrict__ v_prev, const Rd8& rd,
                                         const i32x8& pin, i32x8& pout, float& alpha, float c,
@@ -214,7 +218,8 @@ __device__ __forceinline__ bool steady8(State8& st, const char* __restrict__ k_c
   f32x16 s[2];
   scores8(s, k_cur, rd, st);
   if (masked) mask8(s, lim);
-  float mref = 0.f, msub = 0.f, rs = 0.f;
+  float rs = 0.f;
+  i32x8 pk;
   i32x8 va = rd.v(v_prev, 0);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
@@ -222,42 +227,33 @@ __device__ __forceinline__ bool steady8(State8& st, const char* __restrict__ k_c
     if (dt < 3) va = rd.v(v_prev, dt + 1);
     st.o[dt] = mfma_fp8(vcur, pin, st.o[dt]);
     __builtin_amdgcn_sched_barrier(0);
-    if (dt == 0) {
-      float mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+    for (int w = 2 * dt; w < 2 * dt + 2; ++w) {
+      float pr[4];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt][v]);
-      const float mx_c = halfwave_max(mx) * c;
-      mref = (mx_c > st.mc + kRescaleTau) ? mx_c : st.mc;
-      msub = (mref == -INFINITY) ? 0.f : mref;
-      alpha = fast_exp2(st.mc - msub);
-    } else {
-      const int w0 = dt == 1 ? 0 : (dt == 2 ? 3 : 6);
-      const int w1 = dt == 1 ? 3 : (dt == 2 ? 6 : 8);
-#pragma unroll
-      for (int w = w0; w < w1; ++w) {
-        float pr[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int idx = 4 * w + e;
-          pr[e] = fast_exp2(fmaf(s[idx >> 4][idx & 15], c, -msub));
-          rs += pr[e];
-        }
-        int x = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
-        x = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], x, true);
-        pout[w] = x;
-        // keep the conversion in this slice
-        asm volatile("" ::"v"(x));
+      for (int e = 0; e < 4; ++e) {
+        const int idx = 4 * w + e;
+        pr[e] = fast_exp2(fmaf(s[idx >> 4][idx & 15], c, -st.mc));
+        rs += pr[e];
       }
-      asm volatile("" : "+v"(rs));
+      int x = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
+      x = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], x, true);
+      pk[w] = x;
+      // keep the conversion in this slice
+      asm volatile("" ::"v"(x));
     }
+    asm volatile("" : "+v"(rs));
     __builtin_amdgcn_sched_barrier(0);
   }
-  st.l = fmaf(alpha, st.l, rs);
-  const bool moved = mref != st.mc;
-  st.mc = mref;
-  return moved;
+  if (__builtin_expect(__all(rs <= kSumCap), 1)) {
+    pout = pk;
+    st.l += rs;
+    alpha = 1.f;
+    return false;
+  }
+  // the row outgrew its reference (or has none yet): the row-maximum path
+  // on the unchanged scores
+  return softmax8(st, s, pout, alpha, c);
 }
 
 }  // namespace

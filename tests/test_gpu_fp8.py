@@ -159,3 +159,18 @@ def test_fp8_full_size_sampled_heads(fa, causal):
         check(og[b:b + 1, :, h:h + 1], lg[b:b + 1, :, h:h + 1], q8[b:b + 1, :, h:h + 1],
               k8[b:b + 1, :, h:h + 1], v8[b:b + 1, :, h:h + 1], ds, w.scale, causal, True,
               f"b{b} h{h}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_rising_scores_move_the_reference(fa, causal):
+    """Scores that grow along the keys make the rows' references move inside
+    the pipelined key loop (probabilities rounded to E4M3 stay below 2^8)."""
+    import torch
+    say("fp8 rising scores", causal)
+    q8, k8, v8, ds = W.make_rising_fp8(1, 4, 2, 1100, 128, seed=5, wid=WID)
+    scale = 1 / np.sqrt(128)
+    o, lse = fa.attention_fp8(dev_u8(q8), dev_u8(k8), dev_u8(v8), q_descale=ds[0],
+                              k_descale=ds[1], v_descale=ds[2], causal=causal, scale=scale,
+                              out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check(host(o), host(lse), q8, k8, v8, ds, scale, causal, False, f"rising causal={causal}")

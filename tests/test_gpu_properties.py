@@ -206,3 +206,25 @@ def test_error_within_twice_a_plain_bf16_attention(fa):
         err_plain = np.abs(plain_bf16_attention(q, k, v, scale, causal) - ref).max()
         say("causal", causal, "fused", err_gpu, "plain bf16", err_plain)
         assert err_gpu <= 2.0 * err_plain
+
+
+@pytest.mark.parametrize("case", [(1100, False), (1100, True), (2048, True)],
+                         ids=["n1100", "n1100-causal", "n2048-causal-8waves"])
+def test_rising_scores_move_the_reference(fa, case):
+    """Scores that grow along the keys (by about 2 log2 units per 64-key
+    tile) make every row's running maximum pass its reference again and
+    again inside the pipelined key loop, so the probabilities of many steps
+    are taken against a reference that must move: the result still matches
+    the oracle."""
+    import torch
+    import oracle
+    from _gpu_helpers import check_lse, check_o
+    n, causal = case
+    say("rising scores", case)
+    q, k, v = W.make_rising(1, 4, 2, n, 128, seed=3, wid=240)
+    scale = 1 / math.sqrt(128)
+    o, lse = fa.attention(dev_bf16(q), dev_bf16(k), dev_bf16(v), causal=causal, scale=scale,
+                          out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(q, k, v, scale, causal)
+    say("err", check_o(host(o), o_ref, False, str(case)), check_lse(host(lse), l_ref, str(case)))

@@ -152,6 +152,18 @@ def make_dout(q_shape, *, seed=0, wid=0, cu_q=None) -> np.ndarray:
 
 # FP8 inputs: N(0,1) draws times a per-tensor multiplier, cast to E4M3 codes by
 # torch's float8_e4m3fn conversion (nearest, ties to even), with descale =
+def make_rising(batch, heads_q, heads_kv, seqlen, head_dim, *, seed=0, wid=0,
+                lift=4.0, slope=1.0 / 16):
+    """make_fixed's bf16 tensors with a ramp built in: component 0 of every
+    query is ``lift`` and component 0 of key j is ``slope * j``, so every
+    row's scores grow along the keys on top of the N(0,1) terms."""
+    q, k, v = make_fixed(batch, heads_q, heads_kv, seqlen, seqlen, head_dim, seed=seed, wid=wid)
+    q[..., 0] = round_f32_to_bf16_bits(np.float32([lift]))[0]
+    ramp = round_f32_to_bf16_bits(np.float32(slope) * np.arange(seqlen, dtype=np.float32))
+    k[..., 0] = ramp[None, :, None]
+    return q, k, v
+
+
 # 1 / multiplier so that descale * decoded codes is N(0,1)-shaped (times
 # k_mult for K).  The multipliers put the bulk of each tensor in E4M3's normal
 # range; draws are clipped to +-440 first (E4M3's largest finite value is 448).
@@ -182,6 +194,26 @@ def make_fixed_fp8(batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim, *, se
         v[b] = normal_fp8(seed, wid, T_V, v.shape[1:], b)
     descales = tuple(1.0 / FP8_MULT[t] for t in (T_Q, T_K, T_V))
     return q, k, v, descales
+
+
+def make_rising_fp8(batch, heads_q, heads_kv, seqlen, head_dim, *, seed=0, wid=0,
+                    lift=8.0, top=28.0):
+    """make_fixed_fp8's E4M3 codes with a ramp built in: component 0 of every
+    query is ``lift`` and component 0 of key j is ``top * j / seqlen`` (real
+    values, before the per-tensor multipliers), so every row's scores grow
+    along the keys.  Returns (q8, k8, v8, descales)."""
+    import torch
+    q, k, v, ds = make_fixed_fp8(batch, heads_q, heads_kv, seqlen, seqlen, head_dim, seed=seed,
+                                 wid=wid)
+
+    def code(x):
+        x = np.clip(np.asarray(x, np.float32), -440.0, 440.0)
+        return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+    q[..., 0] = code([lift * FP8_MULT[T_Q]])[0]
+    ramp = np.float32(top / seqlen) * np.arange(seqlen, dtype=np.float32)
+    k[..., 0] = code(ramp * np.float32(FP8_MULT[T_K]))[None, :, None]
+    return q, k, v, ds
 
 
 def make_varlen_fp8(lengths_q, lengths_k, heads_q, heads_kv, head_dim, *, seed=0, wid=0):
