@@ -181,6 +181,10 @@ def test_decode_workspace_size(lib):
     # default chunk never needs more than the explicit-chunk formula allows
     for (b, h, n, d) in [(64, 32, 32768, 128), (1, 1, 100, 64), (3, 8, 5000, 128)]:
         assert ws(b, h, n, d, 0) > 0
+    # the default chunk's size covers every kv-head count that divides heads_q:
+    # 64 sequences of 32 query heads with one kv head take 512-key chunks
+    # (64 splits of a 32768-key cache), the most of any divisor
+    assert ws(64, 32, 32768, 128, 0) == ws(64, 32, 32768, 128, 512)
     # invalid sizes give 0
     assert ws(1, 1, 100, 96, 0) == 0
     assert ws(1, 0, 100, 64, 0) == 0
