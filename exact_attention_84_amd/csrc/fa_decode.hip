@@ -283,7 +283,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     sum = wave_sum(sum);
     out_lse = mx + logf(sum);
     const float* op = o_part + (size_t)row * n_splits * D + lane * PER;
-    for (int s = 0; s < n_splits; ++s) {
+    // Four splits at a time, their loads issued together (the loop is bound
+    // by load latency, not bandwidth).  An empty split (LSE = -inf) never
+    // wrote its partial O, so its values are read but not used.
+    constexpr int U = 4;
+    int s = 0;
+    for (; s + U <= n_splits; s += U) {
+      float x[U], v[U][PER];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        x[u] = lp[s + u];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[u][e] = op[(size_t)(s + u) * D + e];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (x[u] == -INFINITY) continue;
+        const float w = expf(x[u] - out_lse);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] += w * v[u][e];
+      }
+    }
+    for (; s < n_splits; ++s) {
       const float x = lp[s];
       if (x == -INFINITY) continue;
       const float w = expf(x - out_lse);
