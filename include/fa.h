@@ -155,8 +155,9 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float
 /*
  * fa_decode_workspace_size -- bytes of float32 scratch that
  * fa_fwd_decode_splitkv needs for these sizes (partial O and LSE of every
- * key chunk).  chunk = 0 selects the built-in chunk size.  Returns 0 for
- * invalid sizes.
+ * key chunk).  chunk = 0 selects the built-in chunk size, which depends on
+ * heads_kv as well; the size returned then covers every heads_kv that
+ * divides heads_q.  Returns 0 for invalid sizes.
  */
 size_t fa_decode_workspace_size(int batch, int heads_q, int max_cache_len, int head_dim,
                                 int chunk);
