@@ -191,6 +191,27 @@ def test_decode_workspace_size(lib):
     assert ws(1, 1, 100, 64, 100) == 0
 
 
+def test_default_chunk_workspace_covers_every_kv_head_count(lib):
+    """fa_decode_workspace_size(..., chunk=0) must be enough for the built-in
+    chunk of every heads_kv dividing heads_q (the policy is not monotone in
+    heads_kv).  Every call below is refused before any device work: the
+    workspace pointer is misaligned, and the size check comes first, so the
+    message tells which check refused it."""
+    ws = lib.fa_decode_workspace_size
+    for (b, hq, n) in [(64, 32, 32768), (3, 8, 5000), (1, 16, 2048), (7, 4, 100000), (5, 32, 777)]:
+        need = ws(b, hq, n, 128, 0)
+        hkvs = [h for h in range(1, hq + 1) if hq % h == 0 and hq // h <= 32]
+        for hkv in hkvs:
+            assert dec(lib, batch=b, hq=hq, hkv=hkv, ncache=n, wsb=need, ws=FAKE + 4) == WORKSPACE
+            assert "aligned" in lib.fa_last_error().decode(), (b, hq, n, hkv)
+        # and no byte is spare: 4 fewer fail the size check for some kv-head count
+        short = []
+        for hkv in hkvs:
+            assert dec(lib, batch=b, hq=hq, hkv=hkv, ncache=n, wsb=need - 4, ws=FAKE + 4) == WORKSPACE
+            short.append("needed" in lib.fa_last_error().decode())
+        assert any(short), (b, hq, n)
+
+
 def kvc(lib, **kw):
     a = dict(q=FAKE, kc=FAKE, vc=FAKE, kn=None, vn=None, lens=FAKE, bt=None, mb=0, page=0, nb=0,
              cos=None, sin=None, rdim=0, mpos=0, inter=0, o=FAKE, lse=FAKE, batch=4, hq=32,
