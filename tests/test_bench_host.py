@@ -122,8 +122,14 @@ def test_source_hash_does_not_depend_on_the_checkout_path(tmp_path):
     import subprocess
     import sys
     dst = tmp_path / "copy"
-    shutil.copytree(ROOT, dst, ignore=shutil.ignore_patterns(".git", "_work", "gpurun_out",
-                                                           "_build", "*.so", "__pycache__"))
+    dst.mkdir()
+    # only what the hash reads: bench.py, its input module, the package
+    # sources and build script, and the public header
+    for f in ("bench.py", "workloads.py"):
+        shutil.copy(os.path.join(ROOT, f), dst / f)
+    shutil.copytree(os.path.join(ROOT, "include"), dst / "include")
+    shutil.copytree(os.path.join(ROOT, "exact_attention_84_amd"), dst / "exact_attention_84_amd",
+                    ignore=shutil.ignore_patterns("_build", "*.so", "__pycache__"))
     code = "import bench; print(bench.kernel_source_hash('fa_fwd.hip'))"
     a = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
     b = subprocess.run([sys.executable, "-c", code], cwd=dst, capture_output=True, text=True)
