@@ -130,11 +130,11 @@ __device__ __forceinline__ void transform_tile(f32x16 (&s)[NKT][NT], const Score
 // or NaN: a row still at r = -inf gives inf or NaN) the reference may stay
 // and the step is done (alpha = 1).  Otherwise the tile's scores, kept
 // unchanged, go through the row-maximum path of softmax_probs, which moves
-// the references.  Either way O and l are
-// accumulated relative to the same r, so the result is the same up to
-// rounding.  Returns whether a row moved its reference (alpha then holds the
-// rescale factors).  A tile that crosses the end of the keys or the diagonal
-// is masked first (`masked`, uniform over the wave; limits as in mask_tile).
+// the references.  Either way O and l are accumulated relative to the same
+// r, so the result is the same up to rounding.  Returns whether a row moved
+// its reference (alpha then holds the rescale factors).  A tile that crosses
+// the end of the keys or the diagonal is masked first (`masked`, uniform over
+// the wave; limits as in mask_tile).
 template <int D, int NT, bool LOCAL, bool XF>
 __device__ __forceinline__ bool steady_step(WaveState<D, NT>& st, const char* __restrict__ k_cur,
                                             const char* __restrict__ v_prev, const LdsRead<D>& rd,

@@ -208,9 +208,8 @@ __device__ __forceinline__ void scores8(f32x16 (&s)[2], const char* __restrict__
 // row maximum; every p is at most the lane's sum of them, so when no sum
 // exceeds kSumCap (and none is inf or NaN) the reference stays and alpha = 1.
 // Otherwise the scores, kept unchanged, go through softmax8, which moves the
-// references.  pout receives P_j; returns
-// whether the row moved its reference (alpha then holds the rescale factor,
-// applied before P_j V_j).
+// references.  pout receives P_j; returns whether the row moved its reference
+// (alpha then holds the rescale factor, applied before P_j V_j).
 __device__ __forceinline__ bool steady8(State8& st, const char* __restrict__ k_cur,
                                         const char* __restrict__ v_prev, const Rd8& rd,
                                         const i32x8& pin, i32x8& pout, float& alpha, float c,
