@@ -19,12 +19,15 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_decode.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_wide.hip", "fa_fwd_fp8.hip", "fa_decode.hip", "fa_bwd.hip"]
 # Per-source code-generation options.  The dK/dV kernel runs one wave per
 # SIMD with its accumulators live across the whole loop; selecting the VGPR
 # form of the MFMA instructions keeps them in place instead of copying them
 # between AGPRs and VGPRs around every product.
-SOURCE_FLAGS = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# The 64-row forward keeps O in AGPRs that only its inline assembly names;
+# its score products must therefore stay in VGPR form as well.
+SOURCE_FLAGS = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "fa_fwd_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 

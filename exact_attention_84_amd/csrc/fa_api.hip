@@ -111,7 +111,7 @@ static fa_status fwd_setup(const void* q, const void* k, const void* v, void* o,
                            int batch, int heads_q, int heads_kv, int seqlen_q, int seqlen_k,
                            int head_dim, float scale, int causal, const int32_t* cu_seqlens_q,
                            const int32_t* cu_seqlens_k, int max_seqlen_q, int max_seqlen_k,
-                           fa_dtype o_dtype, bool ext, fa::FwdParams* p, bool* empty) {
+                           fa_dtype o_dtype, fa::FwdKind kind, fa::FwdParams* p, bool* empty) {
   *empty = false;
   if (!valid_head_dim(head_dim))
     return fail(FA_ERR_HEADDIM, "head_dim %d not supported (64 or 128)", head_dim);
@@ -147,11 +147,12 @@ static fa_status fwd_setup(const void* q, const void* k, const void* v, void* o,
   }
   if ((!k || !v) && (long long)batch * rows_k > 0)
     return fail(FA_ERR_NULL, "k and v must be non-NULL");
-  const int waves = ext ? 4 : fa::fwd_waves(head_dim, varlen, rows_q);
-  const int br = fa::fwd_block_rows(waves);
+  const fa::FwdPlan plan = fa::fwd_plan(kind, head_dim, causal != 0, varlen, rows_q);
+  const int br = plan.block_rows;
   const long long n_qtiles = (rows_q + br - 1) / br;
   // causal query tiles are processed in pairs (heavy with light), per sequence
-  const long long n_items = (causal && !ext) ? (n_qtiles + 1) / 2 : n_qtiles;
+  const long long n_items =
+      (causal && kind != fa::FwdKind::Ext) ? (n_qtiles + 1) / 2 : n_qtiles;
   const long long total = (long long)batch * heads_q * n_items;
   if (total > 0x7fffffffLL) return fail(FA_ERR_SHAPE, "too many query tiles");
   if (total == 0) {
@@ -173,7 +174,8 @@ static fa_status fwd_setup(const void* q, const void* k, const void* v, void* o,
   p->n_qtiles = (int)n_qtiles;
   p->n_items = (int)n_items;
   p->total = (int)total;
-  p->waves = waves;
+  p->waves = plan.waves;
+  p->wide = plan.wide;
   p->c = scale * fa::kLog2eHost;
   p->o_f32 = o_dtype == FA_DTYPE_F32;
   return ok();
@@ -188,7 +190,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   bool empty;
   fa_status s = fwd_setup(q, k, v, o, lse, batch, heads_q, heads_kv, seqlen_q, seqlen_k,
                           head_dim, scale, causal, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                          max_seqlen_k, o_dtype, false, &p, &empty);
+                          max_seqlen_k, o_dtype, fa::FwdKind::Plain, &p, &empty);
   if (s != FA_OK || empty) return s;
   s = check_device();
   if (s != FA_OK) return s;
@@ -211,7 +213,7 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float
   bool empty;
   fa_status s = fwd_setup(q, k, v, o, lse, batch, heads_q, heads_kv, seqlen_q, seqlen_k,
                           head_dim, scale, causal, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                          max_seqlen_k, o_dtype, false, &p, &empty);
+                          max_seqlen_k, o_dtype, fa::FwdKind::Fp8, &p, &empty);
   if (s != FA_OK || empty) return s;
   const float c = scale * q_descale * k_descale * fa::kLog2eHost;
   if (!isfinite(c) || !(c > 0.f)) return fail(FA_ERR_ARG, "scale * q_descale * k_descale out of range");
@@ -239,7 +241,7 @@ fa_status fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float
   bool empty;
   fa_status s = fwd_setup(q, k, v, o, lse, batch, heads_q, heads_kv, seqlen_q, seqlen_k,
                           head_dim, scale, causal, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                          max_seqlen_k, o_dtype, true, &p, &empty);
+                          max_seqlen_k, o_dtype, fa::FwdKind::Ext, &p, &empty);
   if (s != FA_OK || empty) return s;
   s = check_device();
   if (s != FA_OK) return s;

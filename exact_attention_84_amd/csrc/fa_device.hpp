@@ -207,6 +207,33 @@ __device__ __forceinline__ void softmax_update(WaveState<D, NT>& st, f32x16 (&s)
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+// One direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l writes lds_dst + 16 l.  Issued as inline assembly, so that the
+// compiler does not make every later LDS read wait for all such loads (it
+// cannot tell the stages apart); the kernel waits for exactly the loads a
+// step needs and then meets at a barrier.  M0 holds the wave's LDS
+// destination; the load reads M0 one wait state after it is set.
+__device__ __forceinline__ void dma16(const void* g, char* lds_dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds_dst)));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(m0) : "memory", "m0");
+}
+
+// The same load with a wave-uniform 64-bit base in SGPRs and a per-lane
+// 32-bit byte offset: the address is base + offset, with no vector address
+// arithmetic per load.
+// lds_addr is the destination's LDS byte address (wave-uniform).
+__device__ __forceinline__ void dma16_s(uint32_t off, const void* base, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(lds_addr) : "memory", "m0");
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)p));
+}
+
 template <int D, int BC, int NW>
 struct TileDMA {
   static constexpr int CPR = D / 8;           // 16-byte chunks per row
@@ -217,6 +244,7 @@ struct TileDMA {
 
   int off[PER_WAVE];  // element offset, from the tile's first row, of the
                       // chunk this lane fills in each of its instructions
+  uint32_t obytes[PER_WAVE];  // the same in bytes (scalar-base loads)
 
   __device__ __forceinline__ static int row_of(int n, int wave, int lane) {
     return dma_row<D>(wave + n * NW, lane);
@@ -227,6 +255,7 @@ struct TileDMA {
     for (int n = 0; n < PER_WAVE; ++n) {
       const int row = row_of(n, wave, lane);
       off[n] = row * (int)row_stride + (dma_chunk<D>(wave + n * NW, lane) << 3);
+      obytes[n] = 2u * (uint32_t)off[n];
     }
   }
 
@@ -249,6 +278,32 @@ struct TileDMA {
             base + (size_t)src * row_stride + (dma_chunk<D>(wave + n * NW, lane) << 3);
         __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds + (wave + n * NW) * 1024), 16, 0,
                                          0);
+      }
+    }
+  }
+
+  // The same loads issued as inline assembly: the caller waits for them
+  // itself (s_waitcnt vmcnt) before the barrier that precedes any read.  A
+  // whole tile takes the scalar-base form (dma16_s; the byte offsets 2 off[n]
+  // fit 32 bits for any tile of one sequence), a tile that runs past klast
+  // the per-lane address form with its rows clamped.
+  // lds_addr is the tile's LDS byte address; `lds` the same place as a pointer.
+  __device__ __forceinline__ void issue_asm(const uint16_t* __restrict__ base, size_t row_stride,
+                                            int k0, int klast, char* lds, uint32_t lds_addr,
+                                            int wave, int lane) const {
+    const uint16_t* tile = base + (size_t)k0 * row_stride;
+    if (k0 + BC - 1 <= klast) {
+#pragma unroll
+      for (int n = 0; n < PER_WAVE; ++n)
+        dma16_s(obytes[n], tile, lds_addr + (wave + n * NW) * 1024);
+    } else {
+#pragma unroll
+      for (int n = 0; n < PER_WAVE; ++n) {
+        const int row = row_of(n, wave, lane);
+        const int src = min(k0 + row, klast);
+        const uint16_t* g =
+            base + (size_t)src * row_stride + (dma_chunk<D>(wave + n * NW, lane) << 3);
+        dma16(g, lds + (wave + n * NW) * 1024);
       }
     }
   }

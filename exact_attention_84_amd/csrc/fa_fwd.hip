@@ -676,11 +676,26 @@ static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-int fwd_waves(int head_dim, bool varlen, int seqlen_q) {
-  return (head_dim == 128 && !varlen && seqlen_q >= 2048) ? 8 : 4;
+// Kernel and workgroup shape of a call.  Non-causal plain attention at head
+// dim 128 runs the 64-row-wave kernel: 4 waves (256 rows) for fixed-length
+// batches of at least 1024 queries, else 2 (128 rows: less padding and more
+// workgroups for short or packed sequences).  Causal calls keep the 32-row
+// waves at two waves per SIMD: at the diagonal, where the waves of a
+// workgroup run out of key tiles at different times, the second wave of a
+// SIMD keeps its matrix core busy, and these kernels measured 5-7 % faster
+// on every causal workload.  The 32-row kernels (also head dim 64, the
+// score variants and FP8) take 8 waves (256 rows, half the K/V loads per
+// query) for fixed-length batches of at least 2048 queries at head dim 128,
+// else 4.
+FwdPlan fwd_plan(FwdKind kind, int head_dim, bool causal, bool varlen, int seqlen_q) {
+  if (kind == FwdKind::Plain && head_dim == 128 && !causal) {
+    const int w = (!varlen && seqlen_q >= 1024) ? 4 : 2;
+    return {w, w * 64, 1};
+  }
+  if (kind == FwdKind::Ext) return {4, 4 * 32 * kFwdNT, 0};
+  const int w = (head_dim == 128 && !varlen && seqlen_q >= 2048) ? 8 : 4;
+  return {w, w * 32 * kFwdNT, 0};
 }
-
-int fwd_block_rows(int waves) { return waves * 32 * kFwdNT; }
 
 template <int D, int NW>
 static hipError_t launch_dw(const FwdParams& p, bool causal, hipStream_t stream) {
@@ -714,6 +729,7 @@ hipError_t launch_fwd_xf(const FwdParams& p, int head_dim, bool causal, int win_
 
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, hipStream_t stream) {
   if (head_dim == 64) return launch_dw<64, 4>(p, causal, stream);
+  if (p.wide) return launch_fwd_wide(p, causal, stream);
   return p.waves == 8 ? launch_dw<128, 8>(p, causal, stream)
                       : launch_dw<128, 4>(p, causal, stream);
 }

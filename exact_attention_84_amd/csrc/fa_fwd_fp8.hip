@@ -40,19 +40,6 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// One direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4):
-// lane l writes lds_dst + 16 l.  Issued as inline assembly, so that the
-// compiler does not make every later LDS read wait for all such loads (it
-// cannot tell the stages apart); the kernel waits for exactly the loads a
-// step needs (wait_tiles_upto) and then meets at a barrier.  M0 holds the
-// wave's LDS destination; the load reads M0 one wait state after it is set.
-__device__ __forceinline__ void dma16(const void* g, char* lds_dst) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds_dst)));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(m0) : "memory", "m0");
-}
-
 // Direct global->LDS fill of one 64-row FP8 tile: 8 wave instructions of
 // 64 x 16 bytes, NW waves issuing 8 / NW each.  Rows past klast are read from
 // row klast (their scores are masked, so they only meet zero probabilities).

@@ -35,7 +35,8 @@ struct FwdParams {
   int n_items;             // workgroups per (sequence, head): n_qtiles, or
                            // ceil(n_qtiles / 2) when causal tiles are paired
   int total;               // workgroups
-  int waves;               // waves per workgroup (4 or 8)
+  int waves;               // waves per workgroup
+  int wide;                // 1: the 64-row-wave kernel (head dim 128), 0: 32-row waves
   float c;                 // scale * log2(e); 1 where scores arrive in log2 units
   int o_f32;
 };
@@ -77,10 +78,6 @@ struct AppendParams {
   int batch, hq, hkv, cache_len;
 };
 
-// Waves per prefill workgroup: 8 (256 query rows, half the K/V loads per
-// query) for fixed-length batches of at least 2048 queries at head_dim 128,
-// else 4 (128 rows; less padding and more workgroups for short or packed
-// sequences).
 // Backward.  The workspace holds two fp32 arrays [Hq][rows_cap + pad]:
 // D = rowsum(dO * O) and LSE * log2(e), head-major so that a lane can read
 // four consecutive query rows at once.
@@ -115,9 +112,17 @@ int bwd_dq_rows();       // query rows per dQ workgroup
 int bwd_dkdv_keys();     // keys per dK/dV workgroup
 hipError_t launch_bwd(const BwdParams& p, int head_dim, bool causal, hipStream_t stream);
 
-int fwd_waves(int head_dim, bool varlen, int seqlen_q);
-int fwd_block_rows(int waves);
+// Which forward kernel a call runs, and its workgroup shape.
+enum class FwdKind { Plain, Ext, Fp8 };
+struct FwdPlan {
+  int waves;       // waves per workgroup
+  int block_rows;  // query rows per workgroup tile
+  int wide;        // 64 query rows per wave
+};
+FwdPlan fwd_plan(FwdKind kind, int head_dim, bool causal, bool varlen, int seqlen_q);
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, hipStream_t stream);
+// Head dim 128, plain attention: 64 query rows per wave (p.waves = 2 or 4).
+hipError_t launch_fwd_wide(const FwdParams& p, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream);
 // FP8 forward (head dim 128): p.c = scale * q_descale * k_descale * log2(e).
 hipError_t launch_fwd_fp8(const FwdParams& p, bool causal, float v_descale, hipStream_t stream);
