@@ -40,6 +40,28 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "exact_attention_84_amd", "csrc")
 
 
+def device_mfma_peak(torch_cus: int):
+    """Dense bf16 MFMA peak of device 0 from its CU count and peak shader clock
+    (hipDeviceGetAttribute), at 4096 flop per clock per CU (four SIMDs, one
+    32x32x16 product per 32 clocks each): (TFLOP/s, CUs, MHz), or None when
+    the runtime's answer does not check out against torch's CU count."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        val = ctypes.c_int(0)
+        # hipDeviceAttributeClockRate (kHz) and hipDeviceAttributeMultiprocessorCount
+        # in ROCm 7.2's hip_runtime_api.h
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), 63, 0) != 0 or val.value != torch_cus:
+            return None
+        cus = val.value
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), 5, 0) != 0 or val.value <= 0:
+            return None
+        mhz = val.value / 1000.0
+        return round(cus * 4096 * mhz * 1e6 / 1e12, 1), cus, mhz
+    except OSError:  # pragma: no cover
+        return None
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -89,7 +111,7 @@ def kernel_source_hash(unit: str = "fa_fwd.hip", csrc: str = CSRC) -> str:
 
 # kernel-name pattern -> (traffic.json tag, translation unit)
 TRAFFIC_KERNELS = {
-    "fwd_kernel<128, 8, 1, false, false>": ("fwd_noncausal_d128", "fa_fwd.hip"),
+    "fwd_wide_kernel<4, false, false>": ("fwd_noncausal_d128", "fa_fwd_wide.hip"),
     "fwd_kernel<128, 8, 1, true, true>": ("fwd_causal_d128", "fa_fwd.hip"),
     "decode_kernel<128>": ("decode_d128", "fa_decode.hip"),
     "bwd_dkdv_kernel<128, false>": ("bwd_dkdv_noncausal_d128", "fa_bwd.hip"),
@@ -108,6 +130,10 @@ def measured_traffic(tag: str):
         return None
     k = t.get("kernels", {}).get(tag)
     if k is None or k.get("source_hash") != kernel_source_hash(k.get("unit", "")):
+        return None
+    # counters of another kernel (a different instance, or an old tag) do not count
+    if not any(t_ == tag and pat in k.get("kernel", "") and u == k.get("unit")
+               for pat, (t_, u) in TRAFFIC_KERNELS.items()):
         return None
     return k.get("bytes_per_launch")
 
@@ -453,36 +479,143 @@ def probe(fa, w, steps, warmup):
         f"{steps} copies of {a.numel() * 4} bytes")
 
 
-def cpu_baseline(w, budget_s=15.0):
-    """The fp64 oracle on (sequence, head) slices of the workload, both modes,
-    taken in order over every sequence and head (wrapping around) until at
-    least ``budget_s`` seconds of CPU work are done."""
-    import oracle
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        return None
+
+
+def _peak_rss_mib():
+    import resource
+    return round(resource.getrusage(resource.RUSAGE_SELF).ru_maxrss / 1024.0, 1)  # KiB on Linux
+
+
+def _oracle_slices(w, budget_s, step):
+    """Runs step(i) -> (work units) for i = 0, 1, ... until budget_s seconds of
+    work are done (at least one call); returns (units, calls, seconds)."""
+    done, n = 0.0, 0
+    t0 = time.perf_counter()
+    while n == 0 or time.perf_counter() - t0 < budget_s:
+        done += step(n)
+        n += 1
+    return done, n, time.perf_counter() - t0
+
+
+def cpu_baseline(w, budget_s=8.0, per_config_s=3.0):
+    """The fp64 oracle timed on this host.  The headline figure is the
+    workload bench.py times, on (sequence, head) slices in both modes, taken
+    in order over every sequence and head (wrapping around) until
+    ``budget_s`` seconds are done.  ``per_config`` times the other workloads
+    the same way on slices of a few seconds each: the single head in full,
+    heads of the long GQA sequence, (sequence, head) pairs of the packed
+    batch, and (sequence, kv head) groups of the decode batch (whose caches
+    are drawn one sequence at a time, never whole)."""
+    import oracle
+    per = {}
+
+    # batched MHA (the headline): both modes per (sequence, head)
     inp = W.make_workload(w, seed=0)
     g = w.heads_q // w.heads_kv
     slices = [(b, h) for b in range(w.batch) for h in range(w.heads_q)]
-    done_flops, n = 0.0, 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
+
+    def mha(n):
         b, h = slices[n % len(slices)]
         qh = oracle.to_f64(inp["q"][b, :, h])
         kh = oracle.to_f64(inp["k"][b, :, h // g])
         vh = oracle.to_f64(inp["v"][b, :, h // g])
+        fl = 0.0
         for causal in (False, True):
             oracle.head_attention(qh, kh, vh, w.scale, causal)
-            done_flops += (0.5 if causal else 1.0) * 4.0 * w.seqlen_q * w.seqlen_k * w.head_dim
-        n += 1
-    dt = time.perf_counter() - t0
-    return {"value": round(done_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            fl += (0.5 if causal else 1.0) * 4.0 * w.seqlen_q * w.seqlen_k * w.head_dim
+        return fl
+
+    done, n, dt = _oracle_slices(w, budget_s, mha)
+    head = {"value": round(done / dt / 1e12, 6), "unit": "TFLOP/s",
             "sample": f"{n} (sequence, head) slices of the {len(slices)} in {w.name} "
-                      f"(batch-major order), each non-causal and causal, fp64 numpy, "
-                      f"{dt:.1f} s"}
+                      f"(batch-major order), each non-causal and causal, {dt:.1f} s"}
+    per[w.name] = head
+    del inp
+
+    # single head: the whole call
+    w1 = W.WORKLOADS[1]
+    i1 = W.make_workload(w1, seed=0)
+    done, n, dt = _oracle_slices(
+        w1, min(1.0, per_config_s),
+        lambda _: (oracle.attention(i1["q"], i1["k"], i1["v"], w1.scale, w1.causal),
+                   W.flops(w1))[1])
+    per[w1.name] = {"value": round(done / dt / 1e12, 6), "unit": "TFLOP/s",
+                    "sample": f"the whole call, {n} times, {dt:.1f} s"}
+
+    # long causal GQA: whole query heads
+    w3 = W.WORKLOADS[3]
+    i3 = W.make_workload(w3, seed=0)
+    g3 = w3.heads_q // w3.heads_kv
+
+    def gqa(n):
+        h = n % w3.heads_q
+        oracle.head_attention(oracle.to_f64(i3["q"][0, :, h]), oracle.to_f64(i3["k"][0, :, h // g3]),
+                              oracle.to_f64(i3["v"][0, :, h // g3]), w3.scale, True)
+        return 0.5 * 4.0 * w3.seqlen_q * w3.seqlen_k * w3.head_dim
+
+    done, n, dt = _oracle_slices(w3, per_config_s, gqa)
+    per[w3.name] = {"value": round(done / dt / 1e12, 6), "unit": "TFLOP/s",
+                    "sample": f"{n} of its {w3.heads_q} query heads, causal, {dt:.1f} s"}
+    del i3
+
+    # packed batch: (sequence, head) pairs, causal within each sequence
+    w4 = W.WORKLOADS[4]
+    i4 = W.make_workload(w4, seed=0)
+    g4 = w4.heads_q // w4.heads_kv
+    cu = i4["cu_q"]
+    pairs = [(s, h) for s in range(w4.batch) for h in range(0, w4.heads_q, g4)]
+
+    def packed(n):
+        s_, h = pairs[n % len(pairs)]
+        a, b = int(cu[s_]), int(cu[s_ + 1])
+        oracle.head_attention(oracle.to_f64(i4["q"][a:b, h]), oracle.to_f64(i4["k"][a:b, h // g4]),
+                              oracle.to_f64(i4["v"][a:b, h // g4]), w4.scale, True)
+        return 0.5 * 4.0 * (b - a) * (b - a) * w4.head_dim
+
+    done, n, dt = _oracle_slices(w4, per_config_s, packed)
+    per[w4.name] = {"value": round(done / dt / 1e12, 6), "unit": "TFLOP/s",
+                    "sample": f"{n} (sequence, head) pairs of its {w4.batch * w4.heads_q}, "
+                              f"sequence-major, one head per kv group, {dt:.1f} s"}
+    del i4
+
+    # split-KV decode: (sequence, kv head) groups, each sequence's cache drawn alone
+    w5 = W.WORKLOADS[5]
+    lens = W.workload_lengths(w5, 0)
+    q5 = W.decode_q(w5.batch, w5.heads_q, w5.head_dim, seed=0, wid=w5.wid)
+    g5 = w5.heads_q // w5.heads_kv
+    cache = {}
+
+    def dec(n):
+        b = (n // w5.heads_kv) % w5.batch
+        kvh = n % w5.heads_kv
+        if b not in cache:
+            cache.clear()
+            cache[b] = W.decode_kv_slice(b, int(lens[b]), w5.heads_kv, w5.head_dim, seed=0,
+                                         wid=w5.wid)
+        kb, vb = cache[b]
+        kf, vf = oracle.to_f64(kb[:, kvh]), oracle.to_f64(vb[:, kvh])
+        for h in range(kvh * g5, (kvh + 1) * g5):
+            oracle.head_attention(oracle.to_f64(q5[b, h])[None, :], kf, vf, w5.scale, False)
+        return 2.0 * int(lens[b]) * w5.head_dim * 2  # K and V rows of the group, bf16
+
+    done, n, dt = _oracle_slices(w5, per_config_s, dec)
+    per[w5.name] = {"value": round(done / dt / 1e9, 4), "unit": "GB/s",
+                    "sample": f"{n} (sequence, kv head) groups of its {w5.batch * w5.heads_kv}, "
+                              f"each with its {g5} query heads, {dt:.1f} s "
+                              f"(including drawing each sequence's cache)"}
+    threads = _blas_threads()
+    return {"value": head["value"], "unit": "TFLOP/s",
+            # the matrix products run on the BLAS threads, the rest on one
+            "cores": threads if threads else 1, "host_cpus": os.cpu_count(),
+            "blas_threads": threads, "kind": "oracle",
+            "sample": head["sample"] + ", fp64 numpy", "peak_rss_mib": _peak_rss_mib(),
+            "per_config": per}
 
 
 def main():
@@ -517,6 +650,8 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log("device", props.name, getattr(props, "gcnArchName", ""), "CUs",
         props.multi_processor_count)
+    dev_peak = device_mfma_peak(props.multi_processor_count)
+    log("bf16 MFMA peak from the device", dev_peak, "against the published", PEAK_BF16_TFLOPS)
 
     w = W.WORKLOADS[2]
     if a.probe:
@@ -566,7 +701,7 @@ def main():
     log(f"step {ms_step:.4f} ms ({wall / a.steps * 1e3:.4f} ms wall), non-causal {ms_nc:.4f} ms "
         f"({ach:.1f} TFLOP/s), causal {ms_c:.4f} ms ({fl_c / (ms_c * 1e-3) / 1e12:.1f} TFLOP/s)")
 
-    kname = "fwd_kernel<128, 8, 1, false, false>"
+    kname = "fwd_wide_kernel<4, false, false>"
     traffic = measured_traffic("fwd_noncausal_d128")
     res = {
         "metric": METRIC,
@@ -588,6 +723,8 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "kernel": kname, "achieved": round(ach, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "device_peak": ({"tflops": dev_peak[0], "cus": dev_peak[1],
+                                      "max_clock_mhz": dev_peak[2]} if dev_peak else None),
                      "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "avg_launch_ms": round(ms_nc, 5),
                      "flop_per_launch": fl_nc},

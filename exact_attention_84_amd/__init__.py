@@ -23,9 +23,20 @@ __all__ = ["attention", "attention_fp8", "decode", "combine", "decode_workspace_
 _OUT_DTYPES = {torch.bfloat16: FA_DTYPE_BF16, torch.float32: FA_DTYPE_F32}
 
 
+def _stream(stream):
+    return torch.cuda.current_stream() if stream is None else stream
+
+
 def _stream_handle(stream) -> int:
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    return _stream(stream).cuda_stream
+
+
+def _empty(shape, dtype, device, stream):
+    """A new tensor owned by the stream the library's kernels run on, so that
+    torch's caching allocator cannot hand its memory to work on another stream
+    while those kernels still use it."""
+    with torch.cuda.stream(_stream(stream)):
+        return torch.empty(shape, dtype=dtype, device=device)
 
 
 def _ptr(t):
@@ -96,13 +107,13 @@ def attention(q, k, v, *, causal: bool = False, scale: float | None = None,
         max_seqlen_q = max_seqlen_k = 0
         lse_shape = (batch, nq, hq)
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+        out = _empty(q.shape, out_dtype, q.device, stream)
     else:
         _need(out, "out", out_dtype, ndim)
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
     if lse is None:
-        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+        lse = _empty(lse_shape, torch.float32, q.device, stream)
     else:
         _need(lse, "lse", torch.float32)
         if tuple(lse.shape) != lse_shape:
@@ -182,13 +193,13 @@ def attention_fp8(q, k, v, *, q_descale: float = 1.0, k_descale: float = 1.0,
         max_seqlen_q = max_seqlen_k = 0
         lse_shape = (batch, nq, hq)
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+        out = _empty(q.shape, out_dtype, q.device, stream)
     else:
         _need(out, "out", out_dtype, ndim)
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
     if lse is None:
-        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+        lse = _empty(lse_shape, torch.float32, q.device, stream)
     else:
         _need(lse, "lse", torch.float32)
         if tuple(lse.shape) != lse_shape:
@@ -246,12 +257,12 @@ def attention_backward(q, k, v, out, lse, dout, *, causal: bool = False,
         raise ValueError(f"lse must have shape {lse_shape}")
     need = lib.fa_bwd_workspace_size(batch, hq, rows_q)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = _empty(max(need, 16), torch.uint8, q.device, stream)
     else:
         _need(workspace, "workspace", torch.uint8)
-    dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
-    dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device)
-    dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
+    dq = _empty(q.shape, grad_dtype, q.device, stream)
+    dk = _empty(k.shape, grad_dtype, q.device, stream)
+    dv = _empty(v.shape, grad_dtype, q.device, stream)
     st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq),
                     _ptr(dk), _ptr(dv), batch, hq, hkv, nq, nk, d, scale, int(bool(causal)),
                     _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), int(max_seqlen_q), int(max_seqlen_k),
@@ -294,17 +305,21 @@ def decode(q, k_cache, v_cache, cache_seqlens, *, scale: float | None = None, ch
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     need = lib.fa_decode_workspace_size(batch, hq, ncache, d, chunk)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = _empty(max(need, 16), torch.uint8, q.device, stream)
     else:
         _need(workspace, "workspace", torch.uint8)
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+        out = _empty(q.shape, out_dtype, q.device, stream)
     else:
         _need(out, "out", out_dtype, 3)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
     if lse is None:
-        lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
+        lse = _empty((batch, hq), torch.float32, q.device, stream)
     else:
         _need(lse, "lse", torch.float32, 2)
+        if tuple(lse.shape) != (batch, hq):
+            raise ValueError(f"lse must have shape {(batch, hq)}")
     st = lib.fa_fwd_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
                                    _ptr(out), _ptr(lse), batch, hq, hkv, ncache, d, scale,
                                    int(chunk), _ptr(workspace), workspace.numel(),
@@ -319,19 +334,9 @@ def decode_kvcache_workspace_size(batch: int, heads_q: int, max_cache_len: int, 
                                                        chunk))
 
 
-def decode_kvcache(q, k_cache, v_cache, cache_seqlens, *, k_new=None, v_new=None,
-                   block_table=None, rotary_cos=None, rotary_sin=None,
-                   rotary_interleaved: bool = False, scale: float | None = None, chunk: int = 0,
-                   out=None, lse=None, workspace=None, out_dtype=torch.bfloat16, stream=None):
-    """One decode step that updates the cache in place (``fa_fwd_decode_kvcache``).
-
-    q [B, Hq, d]; k_new/v_new [B, Hkv, d] or None; cache_seqlens int32 [B]
-    (tokens cached before the call; not modified).  Contiguous caches are
-    [B, Ncache, Hkv, d]; with ``block_table`` (int32 [B, max_blocks]) they are
-    paged [num_blocks, page_size, Hkv, d].  ``rotary_cos``/``rotary_sin`` are
-    fp32 [max_pos, rotary_dim / 2].  Returns (o [B, Hq, d], lse [B, Hq]).
-    """
-    lib = load()
+def _kvcache_args(q, k_cache, v_cache, cache_seqlens, k_new, v_new, block_table, rotary_cos,
+                  rotary_sin, out_dtype):
+    """Checks of a KV-cache decode call; returns its sizes."""
     _need(q, "q", torch.bfloat16, 3)
     _need(k_cache, "k_cache", torch.bfloat16, 4)
     _need(v_cache, "v_cache", torch.bfloat16, 4)
@@ -372,20 +377,46 @@ def decode_kvcache(q, k_cache, v_cache, cache_seqlens, *, k_new=None, v_new=None
         if rotary_cos.shape != rotary_sin.shape:
             raise ValueError("rotary tables differ in shape")
         max_pos, rdim = rotary_cos.shape[0], 2 * rotary_cos.shape[1]
+    return batch, hq, hkv, d, cap, max_blocks, page, num_blocks, rdim, max_pos
+
+
+def _check_out_lse(out, lse, q, out_dtype):
+    batch, hq = q.shape[0], q.shape[1]
+    _need(out, "out", out_dtype, 3)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _need(lse, "lse", torch.float32, 2)
+    if tuple(lse.shape) != (batch, hq):
+        raise ValueError(f"lse must have shape {(batch, hq)}")
+
+
+def decode_kvcache(q, k_cache, v_cache, cache_seqlens, *, k_new=None, v_new=None,
+                   block_table=None, rotary_cos=None, rotary_sin=None,
+                   rotary_interleaved: bool = False, scale: float | None = None, chunk: int = 0,
+                   out=None, lse=None, workspace=None, out_dtype=torch.bfloat16, stream=None):
+    """One decode step that updates the cache in place (``fa_fwd_decode_kvcache``).
+
+    q [B, Hq, d]; k_new/v_new [B, Hkv, d] or None; cache_seqlens int32 [B]
+    (tokens cached before the call; not modified).  Contiguous caches are
+    [B, Ncache, Hkv, d]; with ``block_table`` (int32 [B, max_blocks]) they are
+    paged [num_blocks, page_size, Hkv, d].  ``rotary_cos``/``rotary_sin`` are
+    fp32 [max_pos, rotary_dim / 2].  Returns (o [B, Hq, d], lse [B, Hq]).
+    """
+    lib = load()
+    batch, hq, hkv, d, cap, max_blocks, page, num_blocks, rdim, max_pos = _kvcache_args(
+        q, k_cache, v_cache, cache_seqlens, k_new, v_new, block_table, rotary_cos, rotary_sin,
+        out_dtype)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     need = lib.fa_decode_kvcache_workspace_size(batch, hq, cap, d, chunk)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = _empty(max(need, 16), torch.uint8, q.device, stream)
     else:
         _need(workspace, "workspace", torch.uint8)
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
-    else:
-        _need(out, "out", out_dtype, 3)
+        out = _empty(q.shape, out_dtype, q.device, stream)
     if lse is None:
-        lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
-    else:
-        _need(lse, "lse", torch.float32, 2)
+        lse = _empty((batch, hq), torch.float32, q.device, stream)
+    _check_out_lse(out, lse, q, out_dtype)
     st = lib.fa_fwd_decode_kvcache(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(cache_seqlens),
         _ptr(block_table), max_blocks, page, num_blocks, _ptr(rotary_cos), _ptr(rotary_sin), rdim,
@@ -405,10 +436,20 @@ def combine(o_part, lse_part, *, out=None, lse=None, out_dtype=torch.float32, st
     rows, n_splits, d = o_part.shape
     if tuple(lse_part.shape) != (rows, n_splits):
         raise ValueError("lse_part must be [rows, n_splits]")
+    if out_dtype not in _OUT_DTYPES:
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
     if out is None:
-        out = torch.empty((rows, d), dtype=out_dtype, device=o_part.device)
+        out = _empty((rows, d), out_dtype, o_part.device, stream)
+    else:
+        _need(out, "out", out_dtype, 2)
+        if tuple(out.shape) != (rows, d):
+            raise ValueError(f"out must have shape {(rows, d)}")
     if lse is None:
-        lse = torch.empty((rows,), dtype=torch.float32, device=o_part.device)
+        lse = _empty((rows,), torch.float32, o_part.device, stream)
+    else:
+        _need(lse, "lse", torch.float32, 1)
+        if tuple(lse.shape) != (rows,):
+            raise ValueError(f"lse must have shape {(rows,)}")
     st = lib.fa_combine(_ptr(o_part), _ptr(lse_part), rows, n_splits, d, _ptr(out), _ptr(lse),
                         _OUT_DTYPES[out_dtype], _stream_handle(stream))
     check(st, "fa_combine")

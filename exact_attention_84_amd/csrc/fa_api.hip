@@ -311,7 +311,8 @@ size_t fa_decode_kvcache_workspace_size(int batch, int heads_q, int max_cache_le
   return qrot_bytes(batch, heads_q, head_dim) + part;
 }
 
-fa_status fa_fwd_decode_kvcache(const void* q, void* k_cache, void* v_cache, const void* k_new,
+// The KV-cache decode step behind fa_fwd_decode_kvcache.
+static fa_status decode_kvcache(const void* q, void* k_cache, void* v_cache, const void* k_new,
                                 const void* v_new, const int32_t* cache_seqlens,
                                 const int32_t* block_table, int max_blocks_per_seq,
                                 int page_size, int num_blocks, const float* rotary_cos,
@@ -320,7 +321,9 @@ fa_status fa_fwd_decode_kvcache(const void* q, void* k_cache, void* v_cache, con
                                 int heads_q, int heads_kv, int max_cache_len, int head_dim,
                                 float scale, int chunk, void* workspace, size_t workspace_bytes,
                                 fa_dtype o_dtype, void* stream) {
-  if (!q || !k_cache || !v_cache || !cache_seqlens || !o || !lse)
+  // An empty batch touches no tensor: its data pointers may be NULL (as
+  // those of empty torch tensors are), and there is nothing to do.
+  if (batch > 0 && (!q || !k_cache || !v_cache || !cache_seqlens || !o || !lse))
     return fail(FA_ERR_NULL, "q, caches, cache_seqlens, o and lse must be non-NULL");
   if ((k_new == nullptr) != (v_new == nullptr))
     return fail(FA_ERR_NULL, "k_new and v_new must both be given or both be NULL");
@@ -362,6 +365,7 @@ fa_status fa_fwd_decode_kvcache(const void* q, void* k_cache, void* v_cache, con
                 rotary_dim);
   if (rotary_interleaved != 0 && rotary_interleaved != 1)
     return fail(FA_ERR_ARG, "rotary_interleaved must be 0 or 1");
+  if (batch == 0) return ok();
   const int c = chunk ? chunk : default_decode_chunk(batch, heads_kv, max_cache_len);
   const int n_splits = decode_splits(max_cache_len, c);
   const size_t qrb = rot ? qrot_bytes(batch, heads_q, head_dim) : 0;
@@ -373,7 +377,6 @@ fa_status fa_fwd_decode_kvcache(const void* q, void* k_cache, void* v_cache, con
     return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
   const long long total = (long long)batch * heads_kv * n_splits;
   if (total > 0x7fffffffLL) return fail(FA_ERR_SHAPE, "too many splits");
-  if (batch == 0) return ok();
 
   fa_status s = check_device();
   if (s != FA_OK) return s;
@@ -433,6 +436,22 @@ fa_status fa_fwd_decode_kvcache(const void* q, void* k_cache, void* v_cache, con
                          o_dtype == FA_DTYPE_F32, st);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+fa_status fa_fwd_decode_kvcache(const void* q, void* k_cache, void* v_cache, const void* k_new,
+                                const void* v_new, const int32_t* cache_seqlens,
+                                const int32_t* block_table, int max_blocks_per_seq,
+                                int page_size, int num_blocks, const float* rotary_cos,
+                                const float* rotary_sin, int rotary_dim, int rotary_max_pos,
+                                int rotary_interleaved, void* o, float* lse, int batch,
+                                int heads_q, int heads_kv, int max_cache_len, int head_dim,
+                                float scale, int chunk, void* workspace, size_t workspace_bytes,
+                                fa_dtype o_dtype, void* stream) {
+  return decode_kvcache(q, k_cache, v_cache, k_new, v_new, cache_seqlens, block_table,
+                        max_blocks_per_seq, page_size, num_blocks, rotary_cos, rotary_sin,
+                        rotary_dim, rotary_max_pos, rotary_interleaved, o, lse, batch, heads_q,
+                        heads_kv, max_cache_len, head_dim, scale, chunk, workspace,
+                        workspace_bytes, o_dtype, stream);
 }
 
 fa_status fa_combine(const float* o_part, const float* lse_part, int rows, int n_splits,

@@ -259,6 +259,15 @@ def test_decode_kvcache_empty_batch_is_noop(lib):
     # nothing to compute: validated, then FA_OK without touching a device
     assert kvc(lib, batch=0, wsb=16) == OK
     assert kvc(lib, batch=0, wsb=16, **PAGED, **ROT) == OK
+    # empty tensors come with NULL data pointers, the workspace too
+    nulls = dict(q=None, kc=None, vc=None, lens=None, o=None, lse=None, ws=None, wsb=0)
+    assert kvc(lib, batch=0, **nulls) == OK
+    assert lib.fa_fwd_decode_splitkv(None, None, None, None, None, None, 0, 32, 8, 4096, 128,
+                                     0.088, 0, None, 0, 0, None) == OK
+    # arguments are still validated
+    assert kvc(lib, batch=0, d=96, **nulls) == HEADDIM
+    # a non-empty batch still needs its pointers
+    assert kvc(lib, batch=1, q=None) == NULL
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -35,7 +35,7 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_write_traffic_scales_by_the_copy_kernel(tmp_path, monkeypatch):
-    nc = "void fa::fwd_kernel<128, 8, 1, false, false>(fa::FwdParams)"
+    nc = "void fa::fwd_wide_kernel<4, false, false>(fa::FwdParams)"
     ca = "void fa::fwd_kernel<128, 8, 1, true, true>(fa::FwdParams)"
     cp = "__amd_rocclr_copyBuffer"
     # the copy moves 2^30 bytes each way; FETCH_SIZE reads half of it (x2),
@@ -56,7 +56,8 @@ def test_write_traffic_scales_by_the_copy_kernel(tmp_path, monkeypatch):
     assert k["bytes_per_launch"] == k["read_bytes"] + k["write_bytes"]
     assert t["kernels"]["fwd_causal_d128"]["read_bytes"] == 500 * 1024 * 2
     assert json.loads(out_file.read_text()) == t
-    assert k["unit"] == "fa_fwd.hip" and k["source_hash"] == bench.kernel_source_hash("fa_fwd.hip")
+    assert (k["unit"] == "fa_fwd_wide.hip"
+            and k["source_hash"] == bench.kernel_source_hash("fa_fwd_wide.hip"))
     # read back only while the kernel's sources are unchanged
     assert bench.measured_traffic("fwd_noncausal_d128") == k["bytes_per_launch"]
     stale = json.loads(json.dumps(t))
@@ -64,6 +65,11 @@ def test_write_traffic_scales_by_the_copy_kernel(tmp_path, monkeypatch):
     out_file.write_text(json.dumps(stale))
     assert bench.measured_traffic("fwd_noncausal_d128") is None
     assert bench.measured_traffic("fwd_causal_d128") is not None
+    # counters of another instance under the same tag are not used either
+    other = json.loads(json.dumps(t))
+    other["kernels"]["fwd_noncausal_d128"]["kernel"] = "void fa::fwd_kernel<128, 8, 1, false, false>"
+    out_file.write_text(json.dumps(other))
+    assert bench.measured_traffic("fwd_noncausal_d128") is None
 
 
 def test_write_traffic_needs_the_copy_kernel(tmp_path, monkeypatch):
