@@ -16,7 +16,7 @@ import math
 
 import torch
 
-from ._lib import FA_DTYPE_BF16, FA_DTYPE_F32, FaError, check, load
+from ._lib import FA_DTYPE_BF16, FA_DTYPE_F32, NOALLOC_SCRATCH_BYTES, FaError, check, load
 
 __all__ = ["attention", "attention_fp8", "decode", "combine", "decode_workspace_size", "FaError", "load"]
 
@@ -424,6 +424,33 @@ def decode_kvcache(q, k_cache, v_cache, cache_seqlens, *, k_new=None, v_new=None
         scale, int(chunk), _ptr(workspace), workspace.numel(), _OUT_DTYPES[out_dtype],
         _stream_handle(stream))
     check(st, "fa_fwd_decode_kvcache")
+    return out, lse
+
+
+def decode_kvcache_noalloc(q, k_cache, v_cache, cache_seqlens, out, lse, *, k_new=None,
+                           v_new=None, block_table=None, rotary_cos=None, rotary_sin=None,
+                           rotary_interleaved: bool = False, scale: float | None = None,
+                           chunk: int = 0, stream=None):
+    """``decode_kvcache`` without any allocation (``fa_fwd_decode_kvcache_noalloc``):
+    the caller passes ``out`` [B, Hq, d] (bf16 or fp32, which sets the output
+    dtype) and ``lse`` fp32 [B, Hq]; the partials live in the library's own
+    per-device scratch of ``NOALLOC_SCRATCH_BYTES``.  Calls that can overlap on
+    one device race on that scratch."""
+    lib = load()
+    if out is None or lse is None:
+        raise ValueError("decode_kvcache_noalloc writes into caller-provided out and lse")
+    out_dtype = out.dtype
+    batch, hq, hkv, d, cap, max_blocks, page, num_blocks, rdim, max_pos = _kvcache_args(
+        q, k_cache, v_cache, cache_seqlens, k_new, v_new, block_table, rotary_cos, rotary_sin,
+        out_dtype)
+    _check_out_lse(out, lse, q, out_dtype)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.fa_fwd_decode_kvcache_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(cache_seqlens),
+        _ptr(block_table), max_blocks, page, num_blocks, _ptr(rotary_cos), _ptr(rotary_sin), rdim,
+        max_pos, int(bool(rotary_interleaved)), _ptr(out), _ptr(lse), batch, hq, hkv, cap, d,
+        scale, int(chunk), _OUT_DTYPES[out_dtype], _stream_handle(stream))
+    check(st, "fa_fwd_decode_kvcache_noalloc")
     return out, lse
 
 

@@ -15,12 +15,14 @@ LIB_PATH = os.environ.get("FA_LIB_PATH", os.path.join(_HERE, "libfa.so"))
 FA_OK = 0
 FA_DTYPE_BF16 = 0
 FA_DTYPE_F32 = 1
+NOALLOC_SCRATCH_BYTES = 64 << 20  # FA_NOALLOC_SCRATCH_BYTES of fa.h
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM",
                 4: "FA_ERR_GQA", 5: "FA_ERR_DTYPE", 6: "FA_ERR_ARCH", 7: "FA_ERR_WORKSPACE",
                 8: "FA_ERR_HIP", 9: "FA_ERR_ARG"}
 EXPORTS = ("fa_fwd", "fa_fwd_ext", "fa_fwd_fp8", "fa_decode_workspace_size",
            "fa_fwd_decode_splitkv",
-           "fa_decode_kvcache_workspace_size", "fa_fwd_decode_kvcache", "fa_combine",
+           "fa_decode_kvcache_workspace_size", "fa_fwd_decode_kvcache",
+           "fa_fwd_decode_kvcache_noalloc", "fa_combine",
            "fa_bwd_workspace_size", "fa_bwd", "fa_status_string", "fa_last_error")
 
 _lib = None
@@ -65,6 +67,9 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_decode_kvcache.argtypes = [P, P, P, P, P, P, P, I, I, I, P, P, I, I, I, P, P, I, I,
                                           I, I, I, F, I, P, ctypes.c_size_t, I, P]
     lib.fa_fwd_decode_kvcache.restype = I
+    lib.fa_fwd_decode_kvcache_noalloc.argtypes = [P, P, P, P, P, P, P, I, I, I, P, P, I, I, I, P,
+                                                  P, I, I, I, I, I, F, I, I, P]
+    lib.fa_fwd_decode_kvcache_noalloc.restype = I
     lib.fa_bwd_workspace_size.argtypes = [I, I, I]
     lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, I, I, I, P,

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_internal.hpp"
@@ -81,6 +82,47 @@ int default_decode_chunk(int batch, int heads_kv, int max_cache_len) {
 int decode_splits(int max_cache_len, int chunk) {
   const int s = (max_cache_len + chunk - 1) / chunk;
   return s < 1 ? 1 : s;
+}
+
+}  // namespace
+
+// Scratch of fa_fwd_decode_kvcache_noalloc: the rotated queries and the
+// split partials.  Every device the library runs on holds its own copy from
+// the moment the code object is loaded there until the process ends.  Host
+// code never names it directly (on the host the name is only a stand-in):
+// it uses the device address that scratch_address() looks up.  Nothing in it
+// has to start at zero: each call writes the partial LSE of every split
+// (-inf for an empty one), reads a partial O only where that LSE is finite,
+// and writes the rotated queries before reading them.
+static __device__ __align__(256) char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::atomic<char*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's copy of `scratch`, looked up once per
+// device (check_device() has validated the device index).
+fa_status scratch_address(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  char* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* a = nullptr;
+      e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !a)
+        return fail(FA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                    hipGetErrorString(e));
+      p = static_cast<char*>(a);
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FA_OK;
 }
 
 }  // namespace
@@ -311,7 +353,9 @@ size_t fa_decode_kvcache_workspace_size(int batch, int heads_q, int max_cache_le
   return qrot_bytes(batch, heads_q, head_dim) + part;
 }
 
-// The KV-cache decode step behind fa_fwd_decode_kvcache.
+// The KV-cache decode step behind fa_fwd_decode_kvcache and its
+// allocation-free variant.  With builtin_scratch the caller's workspace is
+// ignored and the partials go to this device's copy of `scratch`.
 static fa_status decode_kvcache(const void* q, void* k_cache, void* v_cache, const void* k_new,
                                 const void* v_new, const int32_t* cache_seqlens,
                                 const int32_t* block_table, int max_blocks_per_seq,
@@ -320,7 +364,7 @@ static fa_status decode_kvcache(const void* q, void* k_cache, void* v_cache, con
                                 int rotary_interleaved, void* o, float* lse, int batch,
                                 int heads_q, int heads_kv, int max_cache_len, int head_dim,
                                 float scale, int chunk, void* workspace, size_t workspace_bytes,
-                                fa_dtype o_dtype, void* stream) {
+                                bool builtin_scratch, fa_dtype o_dtype, void* stream) {
   // An empty batch touches no tensor: its data pointers may be NULL (as
   // those of empty torch tensors are), and there is nothing to do.
   if (batch > 0 && (!q || !k_cache || !v_cache || !cache_seqlens || !o || !lse))
@@ -370,11 +414,18 @@ static fa_status decode_kvcache(const void* q, void* k_cache, void* v_cache, con
   const int n_splits = decode_splits(max_cache_len, c);
   const size_t qrb = rot ? qrot_bytes(batch, heads_q, head_dim) : 0;
   const size_t need = qrb + fa_decode_workspace_size(batch, heads_q, max_cache_len, head_dim, c);
-  if (!workspace || workspace_bytes < need)
-    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                workspace ? workspace_bytes : (size_t)0);
-  if (reinterpret_cast<uintptr_t>(workspace) % 16)
-    return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  if (builtin_scratch) {
+    if (need > (size_t)FA_NOALLOC_SCRATCH_BYTES)
+      return fail(FA_ERR_WORKSPACE, "this call needs %zu bytes of scratch, more than the "
+                  "%zu of the built-in scratch; call fa_fwd_decode_kvcache with a workspace",
+                  need, (size_t)FA_NOALLOC_SCRATCH_BYTES);
+  } else {
+    if (!workspace || workspace_bytes < need)
+      return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(workspace) % 16)
+      return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  }
   const long long total = (long long)batch * heads_kv * n_splits;
   if (total > 0x7fffffffLL) return fail(FA_ERR_SHAPE, "too many splits");
 
@@ -382,6 +433,10 @@ static fa_status decode_kvcache(const void* q, void* k_cache, void* v_cache, con
   if (s != FA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
+  if (builtin_scratch) {
+    s = scratch_address(&ws);
+    if (s != FA_OK) return s;
+  }
 
   if (rot || k_new) {
     fa::AppendParams a;
@@ -451,7 +506,24 @@ fa_status fa_fwd_decode_kvcache(const void* q, void* k_cache, void* v_cache, con
                         max_blocks_per_seq, page_size, num_blocks, rotary_cos, rotary_sin,
                         rotary_dim, rotary_max_pos, rotary_interleaved, o, lse, batch, heads_q,
                         heads_kv, max_cache_len, head_dim, scale, chunk, workspace,
-                        workspace_bytes, o_dtype, stream);
+                        workspace_bytes, false, o_dtype, stream);
+}
+
+fa_status fa_fwd_decode_kvcache_noalloc(const void* q, void* k_cache, void* v_cache,
+                                        const void* k_new, const void* v_new,
+                                        const int32_t* cache_seqlens,
+                                        const int32_t* block_table, int max_blocks_per_seq,
+                                        int page_size, int num_blocks, const float* rotary_cos,
+                                        const float* rotary_sin, int rotary_dim,
+                                        int rotary_max_pos, int rotary_interleaved, void* o,
+                                        float* lse, int batch, int heads_q, int heads_kv,
+                                        int max_cache_len, int head_dim, float scale, int chunk,
+                                        fa_dtype o_dtype, void* stream) {
+  return decode_kvcache(q, k_cache, v_cache, k_new, v_new, cache_seqlens, block_table,
+                        max_blocks_per_seq, page_size, num_blocks, rotary_cos, rotary_sin,
+                        rotary_dim, rotary_max_pos, rotary_interleaved, o, lse, batch, heads_q,
+                        heads_kv, max_cache_len, head_dim, scale, chunk, nullptr, 0, true,
+                        o_dtype, stream);
 }
 
 fa_status fa_combine(const float* o_part, const float* lse_part, int rows, int n_splits,

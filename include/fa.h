@@ -258,6 +258,47 @@ fa_status fa_fwd_decode_kvcache(const void* q, void* k_cache, void* v_cache,
                                 void* stream);
 
 /*
+ * Bytes of device scratch that fa_fwd_decode_kvcache_noalloc holds on each
+ * device it runs on (64 MiB).
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * fa_fwd_decode_kvcache_noalloc -- fa_fwd_decode_kvcache without a workspace
+ * argument, for callers that cannot allocate device memory at the call: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); the rotated queries and split partials go to
+ * a scratch array that the library holds on every device it runs on, from
+ * the first use there until the process ends.
+ *   Arguments, layouts, results and errors: as fa_fwd_decode_kvcache, less
+ *   workspace / workspace_bytes.  The call is bit-identical to
+ *   fa_fwd_decode_kvcache with the same arguments.
+ *   Limit: fa_decode_kvcache_workspace_size(batch, heads_q, max_cache_len,
+ *   head_dim, chunk) -- for chunk = 0 an upper bound of the need -- must not
+ *   exceed FA_NOALLOC_SCRATCH_BYTES; a call that needs more returns
+ *   FA_ERR_WORKSPACE before touching the device.  (64 sequences x 32 query
+ *   heads x 32768 cache rows x head_dim 128 with the built-in chunk needs
+ *   about 24 MB.)
+ *   Concurrency: every call on one device shares that device's scratch.
+ *   Calls on one stream are ordered and safe; calls that can overlap on one
+ *   device (different streams, or different host threads without ordering)
+ *   race on it and give wrong results.  Nothing in the scratch needs to be
+ *   cleared between calls.
+ */
+fa_status fa_fwd_decode_kvcache_noalloc(const void* q, void* k_cache, void* v_cache,
+                                        const void* k_new, const void* v_new,
+                                        const int32_t* cache_seqlens,
+                                        const int32_t* block_table, int max_blocks_per_seq,
+                                        int page_size, int num_blocks,
+                                        const float* rotary_cos, const float* rotary_sin,
+                                        int rotary_dim, int rotary_max_pos,
+                                        int rotary_interleaved, void* o, float* lse,
+                                        int batch, int heads_q, int heads_kv,
+                                        int max_cache_len, int head_dim, float scale,
+                                        int chunk, fa_dtype o_dtype, void* stream);
+
+/*
  * fa_combine -- LSE-weighted merge of partial results computed over disjoint
  * key subsets (the block merge of the PKU lecture notes "FlashAttention",
  * section 6, written with logsumexps):
