@@ -189,21 +189,30 @@ def to_dev(bits):
 
 class LaunchTimer:
     """HIP-event timing of individual launches on torch's current stream (the
-    stream the library launches on)."""
+    stream the library launches on).  One event is recorded after each launch
+    (and one before the first), so a launch's time runs from the end of the
+    previous launch to its own end: back-to-back launches are timed with one
+    event between them rather than a pair around each, which would add an
+    idle gap per launch."""
 
     def __init__(self):
-        self.pairs = {}
+        self.events = []
+        self.names = []
 
     def run(self, name, fn):
         import torch
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
+        if not self.events:
+            self.events.append(torch.cuda.Event(enable_timing=True))
+            self.events[0].record()
         fn()
-        b.record()
-        self.pairs.setdefault(name, []).append((a, b))
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.events.append(e)
+        self.names.append(name)
 
     def times_ms(self, name):
-        return [a.elapsed_time(b) for a, b in self.pairs.get(name, [])]
+        ev = self.events
+        return [ev[i].elapsed_time(ev[i + 1]) for i, n in enumerate(self.names) if n == name]
 
     def avg_ms(self, name):
         t = self.times_ms(name)

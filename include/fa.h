@@ -154,10 +154,14 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float
 
 /*
  * fa_decode_workspace_size -- bytes of float32 scratch that
- * fa_fwd_decode_splitkv needs for these sizes (partial O and LSE of every
- * key chunk).  chunk = 0 selects the built-in chunk size, which depends on
- * heads_kv as well; the size returned then covers every heads_kv that
- * divides heads_q.  Returns 0 for invalid sizes.
+ * fa_fwd_decode_splitkv needs for these sizes: the partial O and LSE that
+ * every key chunk writes before the LSE-weighted merge ("FlashAttention — IO
+ * 感知的精确注意力 kernel", section 2.3 step 3: split-KV for a short query;
+ * section 7: each split keeps its partial result and a final step combines
+ * them).  Per query row and split it holds head_dim + 1 floats.  chunk = 0
+ * selects the built-in chunk size, which depends on heads_kv as well; the
+ * size returned then covers every heads_kv that divides heads_q.  Returns 0
+ * for invalid sizes.
  */
 size_t fa_decode_workspace_size(int batch, int heads_q, int max_cache_len, int head_dim,
                                 int chunk);
@@ -354,11 +358,21 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  int max_seqlen_k, fa_dtype grad_dtype, void* workspace, size_t workspace_bytes,
                  void* stream);
 
-/* Static, human-readable name of a status code. */
+/*
+ * The error channel of this interface.  No passage of the pages defines
+ * error reporting: these two calls compute nothing of the method and only
+ * describe the status codes the entry points above return.
+ *
+ * fa_status_string -- static, human-readable name of a status code
+ * ("FA_ERR_UNKNOWN" for a value outside fa_status).  Never NULL.
+ */
 const char* fa_status_string(fa_status status);
 
-/* Detail of the last non-FA_OK status returned on the calling thread
- * (empty string if none).  Valid until the next call on that thread. */
+/*
+ * fa_last_error -- detail of the last non-FA_OK status returned on the
+ * calling thread (empty string if none).  The string is owned by the
+ * library, thread-local, and valid until the next call on that thread.
+ */
 const char* fa_last_error(void);
 
 #ifdef __cplusplus
