@@ -181,6 +181,10 @@ static fa_status fwd_setup(const void* q, const void* k, const void* v, void* o,
   if ((long long)batch * rows_q * heads_q * head_dim > kMaxElems ||
       (long long)batch * rows_k * heads_kv * head_dim > kMaxElems)
     return fail(FA_ERR_SHAPE, "tensor too large");
+  // the tile loads form row offsets with 24-bit multiplies
+  if ((long long)heads_kv * head_dim * 2 >= (1LL << 24) ||
+      (long long)heads_q * head_dim * 2 >= (1LL << 24))
+    return fail(FA_ERR_SHAPE, "a token's heads span more than 16 MiB");
   // Pointers are required only for tensors that will be touched: an empty
   // tensor (no query rows, or no keys) may come with a NULL data pointer.
   if (!q || !o || !lse) {

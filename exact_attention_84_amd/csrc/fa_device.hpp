@@ -245,6 +245,11 @@ struct TileDMA {
   int off[PER_WAVE];  // element offset, from the tile's first row, of the
                       // chunk this lane fills in each of its instructions
   uint32_t obytes[PER_WAVE];  // the same in bytes (scalar-base loads)
+  // The swizzle depends on the low four row bits; when consecutive
+  // instructions are 16 rows apart the lane's chunk is the same in all.
+  static constexpr int NCB = (RPI * NW) % 16 == 0 ? 1 : PER_WAVE;
+  int row0;                // the lane's tile row in instruction 0
+  uint32_t cbytes[NCB];    // byte offset of the lane's chunk in its row
 
   __device__ __forceinline__ static int row_of(int n, int wave, int lane) {
     return dma_row<D>(wave + n * NW, lane);
@@ -257,6 +262,9 @@ struct TileDMA {
       off[n] = row * (int)row_stride + (dma_chunk<D>(wave + n * NW, lane) << 3);
       obytes[n] = 2u * (uint32_t)off[n];
     }
+    row0 = row_of(0, wave, lane);
+#pragma unroll
+    for (int n = 0; n < NCB; ++n) cbytes[n] = (uint32_t)dma_chunk<D>(wave + n * NW, lane) << 4;
   }
 
   // Tile rows k0..k0+BC-1 of `base` into `lds`.  Rows past klast are read
@@ -280,6 +288,30 @@ struct TileDMA {
                                          0);
       }
     }
+  }
+
+  // Branch-free form of the same loads, one instruction at a time.  The
+  // scalar base is the tile's first row, or row klast when the whole tile
+  // lies past it; each lane's 32-bit byte offset is its row, clamped to
+  // klast, times the row pitch plus its swizzled chunk.  Every address thus
+  // stays inside rows 0..klast, whatever k0 is.
+  struct Src {
+    const uint16_t* tile;  // first row read
+    int lim;               // last row of the tile that may be read, >= 0
+  };
+  __device__ __forceinline__ static Src src(const uint16_t* __restrict__ base, size_t row_stride,
+                                            int k0, int klast) {
+    const int k = min(k0, klast);
+    return {base + (size_t)k * row_stride, klast - k};
+  }
+  // row_bytes is the row pitch in bytes (2 row_stride), below 2^24.
+  template <int N>
+  __device__ __forceinline__ void issue_one(const Src& s, uint32_t row_bytes, uint32_t lds_addr,
+                                            int wave) const {
+    static_assert(N >= 0 && N < PER_WAVE, "instruction index");
+    const int r = min(row0 + N * RPI * NW, s.lim);
+    dma16_s(__umul24((uint32_t)r, row_bytes) + cbytes[NCB == 1 ? 0 : N], s.tile,
+            lds_addr + (wave + N * NW) * 1024);
   }
 
   // The same loads issued as inline assembly: the caller waits for them
@@ -354,6 +386,17 @@ struct LdsRead {
 };
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Waits for every outstanding vector-memory access through the builtin,
+// whose effect the compiler's wait-count tracking sees (it does not see an
+// asm wait).  Loads the compiler issued before this point (the Q fragments)
+// are then known complete, so it places no waits for them further on.  Such
+// waits would otherwise land inside the key loop, where the hardware counter
+// also counts the asm-issued tile loads, and stall each step on loads issued
+// a few instructions earlier.
+__device__ __forceinline__ void vm_drain() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt not waited on
+}
 
 
 // S^T sub-tiles kt = 0..NKT-1 (keys kt*32..) of a swizzled K tile, with the

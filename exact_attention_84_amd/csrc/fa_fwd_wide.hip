@@ -632,9 +632,31 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
     };
     // Steady periods (both sub-steps steady for this wave), parity static so
     // that every LDS offset is an instruction immediate.  The first one of a
-    // run meets the workgroup at its own start; each one starts the next
-    // one's stage from inside its second sub-step (when that is steady too).
+    // run meets the workgroup at its own start (stage_period).  Each one
+    // meets the workgroup for the next from inside its second sub-step and
+    // there issues the loads of the period after that (K stage J+2, V stage
+    // J+1), a full period ahead of their use.  These loads take no branch
+    // (TileDMA::issue_one): a stage past the last key rereads the last row
+    // into a buffer nobody reads.
     bf16x8 kf0, vf0;
+    constexpr int PW = decltype(dma)::PER_WAVE;
+    const uint32_t kv_row_bytes = 2u * (uint32_t)kv_stride;
+    // instruction n of K stage KS (n < PW) or V stage KS - 1 (n >= PW), into
+    // K buffer KB and V buffer 2 + VB
+    auto load_part = [&](const int KS, auto nc, auto kbuf, auto vbuf)
+        __attribute__((always_inline)) {
+      constexpr int n = decltype(nc)::value;
+      if constexpr (n < PW) {
+        constexpr int KB = decltype(kbuf)::value;
+        const auto src = decltype(dma)::src(kbase, kv_stride, KS * STG, Lk - 1);
+        dma.template issue_one<n>(src, kv_row_bytes, lds_base + KB * STG_BYTES, wave);
+      } else {
+        constexpr int VB = decltype(vbuf)::value;
+        const auto src = decltype(dma)::src(vbase, kv_stride, (KS - 1) * STG, Lk - 1);
+        dma.template issue_one<n - PW>(src, kv_row_bytes, lds_base + (2 + VB) * STG_BYTES,
+                                       wave);
+      }
+    };
     auto steady_period = [&](const int J, auto par, const bool staged, const bool stage_next)
         __attribute__((always_inline)) {
       constexpr int PAR = decltype(par)::value;
@@ -649,10 +671,16 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
       limits(2 * J, lim1);
       limits(2 * J + 1, lim2);
       auto no_stage = [](bf16x8&, bf16x8&) {};
-      // the next period's stage: K stage J+1 and V stage J are in buffers
-      // PAR ^ 1 and PAR
+      // the next period's tiles have landed and every wave is done with this
+      // period's stages: K stage J+1 and V stage J are in buffers PAR ^ 1 and
+      // 2 + PAR; K stage J+2 and V stage J+1 go to buffers PAR and 2 + (PAR ^ 1)
       auto next_stage = [&](bf16x8& kn, bf16x8& vn) __attribute__((always_inline)) {
-        stage_period(J + 1);
+        wait_dma();
+        __syncthreads();
+        auto one = [&](auto nc) __attribute__((always_inline)) {
+          load_part(J + 2, nc, Parity<PAR>{}, Parity<PAR ^ 1>{});
+        };
+        static_for<2 * PW>(one);
         kn = rd.k(lds + (PAR ^ 1) * STG_BYTES, 0, 0);
         vn = rd.v(lds + (2 + PAR) * STG_BYTES, 0, 0, 0);
       };
@@ -666,6 +694,9 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
     const int n_period = n_stage + 1;
     const int last_steady = n_w >= 4 ? (n_w - 2) / 2 : 0;
     general_period(0);
+    // the Q loads are known complete from here on (the first steady period
+    // waits for this period's tile loads anyway)
+    vm_drain();
     int J = 1;
     bool staged = false;
 #pragma clang loop unroll(disable)

@@ -69,6 +69,7 @@ def fwd(lib, **kw):
     (dict(scale=float("nan")), ARG), (dict(causal=2), ARG),
     (dict(odt=2), DTYPE), (dict(odt=-1), DTYPE),
     (dict(cuq=FAKE, mq=-1, mk=10), SHAPE),
+    (dict(hq=65536, hkv=65536), SHAPE),  # a token's heads past 16 MiB
 ])
 def test_fwd_rejects_before_launch(lib, kw, status):
     assert fwd(lib, **kw) == status
