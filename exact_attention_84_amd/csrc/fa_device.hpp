@@ -229,6 +229,15 @@ __device__ __forceinline__ void dma16_s(uint32_t off, const void* base, uint32_t
                :: "v"(off), "s"(base), "s"(lds_addr) : "memory", "m0");
 }
 
+// A pointer that is the same in every lane, moved to scalar registers.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)p));

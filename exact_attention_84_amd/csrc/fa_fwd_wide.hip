@@ -29,6 +29,7 @@
 //
 // Keys move in sub-steps of 32 (one 32x32 score block per row group) and
 // LDS stages of 64 (one barrier per two sub-steps).
+#include <atomic>
 #include <utility>
 
 #include "fa_device.hpp"
@@ -495,84 +496,144 @@ __device__ __forceinline__ void general_sub(int j, int n_w, State& st,
   }
 }
 
-// NW waves of 64 rows per workgroup (one wave per SIMD); PAIR runs two
-// causal query tiles, n-1-i then i, in one workgroup.
+// NW waves of 64 rows per workgroup (one wave per SIMD).  A workgroup runs
+// the query tiles of blocks t = blockIdx.x, blockIdx.x + gridDim.x, ... in
+// turn (the host launches one workgroup per tile, or fewer so that each
+// runs several); PAIR gives each block two causal query tiles, n-1-i then
+// i.  Before a tile's epilogue the workgroup starts the next tile's Q loads
+// and first K stage, so that their latency passes under the epilogue and
+// its stores.
 template <int NW, bool CAUSAL, bool PAIR>
 __device__ __forceinline__ void wide_body(const FwdParams& p) {
   constexpr int BR = NW * 64;
-  // K stages 0 and 1, then V stages 0 and 1
-  __shared__ __attribute__((aligned(1024))) char lds[4 * STG_BYTES];
+  // K stages 0 and 1, V stages 0 and 1, then one 16 KB epilogue area per wave
+  __shared__ __attribute__((aligned(1024))) char lds[4 * STG_BYTES + NW * 16384];
   const uint32_t lds_base = lds_address(lds);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m32 = lane & 31, hh = lane >> 5;
-
-  // ---- work item: (sequence b, kv head, query head in group, query tile) ----
-  const int item = xcd_remap(blockIdx.x, p.total, p.group * p.n_items);
-  const int it = item % p.n_items;
-  int rest = item / p.n_items;
-  const int hg = rest % p.group;
-  rest /= p.group;
-  const int kvh = rest % p.hkv;
-  const int b = rest / p.hkv;
-  const int h = kvh * p.group + hg;
-
-  int q_start, Lq, k_start, Lk;
-  if (p.cu_q) {
-    q_start = p.cu_q[b];
-    Lq = p.cu_q[b + 1] - q_start;
-    k_start = p.cu_k[b];
-    Lk = p.cu_k[b + 1] - k_start;
-  } else {
-    q_start = b * p.seqlen_q;
-    Lq = p.seqlen_q;
-    k_start = b * p.seqlen_k;
-    Lk = p.seqlen_k;
-  }
   const size_t q_stride = (size_t)p.hq * D;
   const size_t kv_stride = (size_t)p.hkv * D;
-  const uint16_t* kbase = p.k + (size_t)k_start * kv_stride + (size_t)kvh * D;
-  const uint16_t* vbase = p.v + (size_t)k_start * kv_stride + (size_t)kvh * D;
-  const int delta = Lk - Lq;  // bottom-right causal offset
 
   TileDMA<D, STG, NW> dma;
   dma.init(kv_stride, wave, lane);
   LdsRead<D> rd;
   rd.init(lane);
 
-  auto run_tile = [&](const int qt) __attribute__((always_inline)) {
-    const int q0 = qt * BR;
-    // 32-key sub-tiles of the workgroup (causal: up to its last row's diagonal)
-    int n_sub = (Lk + SUB - 1) / SUB;
+  // One query tile of one (sequence, query head).
+  struct Tile {
+    int h, q_start, Lq, Lk, qt;
+    const uint16_t* kbase;
+    const uint16_t* vbase;
+  };
+  // Task k of the workgroup: block t = blockIdx.x + (k / TPB) gridDim.x, a
+  // work item (sequence b, kv head, query head in group, query tile i), and
+  // for PAIR its tile n-1-i (k even) or i (k odd).  False when the task has
+  // no rows (past a shorter sequence, or the two tiles of a pair coincide).
+  constexpr int TPB = PAIR ? 2 : 1;
+  auto task = [&](const int k, Tile& T) __attribute__((always_inline)) -> bool {
+    const int t = blockIdx.x + (k / TPB) * gridDim.x;
+    const int item = xcd_remap(t, p.total, p.group * p.n_items);
+    const int it = item % p.n_items;
+    int rest = item / p.n_items;
+    const int hg = rest % p.group;
+    rest /= p.group;
+    const int kvh = rest % p.hkv;
+    const int b = rest / p.hkv;
+    T.h = kvh * p.group + hg;
+    int k_start;
+    if (p.cu_q) {
+      T.q_start = p.cu_q[b];
+      T.Lq = p.cu_q[b + 1] - T.q_start;
+      k_start = p.cu_k[b];
+      T.Lk = p.cu_k[b + 1] - k_start;
+    } else {
+      T.q_start = b * p.seqlen_q;
+      T.Lq = p.seqlen_q;
+      k_start = b * p.seqlen_k;
+      T.Lk = p.seqlen_k;
+    }
+    T.kbase = p.k + (size_t)k_start * kv_stride + (size_t)kvh * D;
+    T.vbase = p.v + (size_t)k_start * kv_stride + (size_t)kvh * D;
+    // every field is the same in all lanes; saying so keeps them in scalar
+    // registers (the tile loads take their base from there)
+    T.h = __builtin_amdgcn_readfirstlane(T.h);
+    T.q_start = __builtin_amdgcn_readfirstlane(T.q_start);
+    T.Lq = __builtin_amdgcn_readfirstlane(T.Lq);
+    T.Lk = __builtin_amdgcn_readfirstlane(T.Lk);
+    T.kbase = uniform_ptr(T.kbase);
+    T.vbase = uniform_ptr(T.vbase);
+    if constexpr (PAIR) {
+      // tile n-1-i (heaviest) then tile i, n counted per sequence, so every
+      // block of a sequence gets about the same work
+      const int first = (T.Lq + BR - 1) / BR - 1 - it;
+      if (first < it) return false;
+      if (k % 2 == 0) {
+        T.qt = first;
+        return true;
+      }
+      T.qt = it;
+      return it < first;
+    } else {
+      T.qt = it;
+      return it * BR < T.Lq;
+    }
+  };
+  // The first task from k on that has rows, or -1 (uniform across the
+  // workgroup: every value involved is).
+  auto next_task = [&](int k, Tile& T) __attribute__((always_inline)) -> int {
+#pragma clang loop unroll(disable)
+    for (;; ++k) {
+      if (blockIdx.x + (k / TPB) * gridDim.x >= p.total) return -1;
+      if (task(k, T)) return k;
+    }
+  };
+  // 32-key sub-tiles of a tile's workgroup (causal: up to its last row's
+  // diagonal), and the 64-key stages that hold them
+  auto tile_subs = [&](const Tile& T) __attribute__((always_inline)) {
+    int n_sub = (T.Lk + SUB - 1) / SUB;
     if (CAUSAL) {
-      const int last_key = min(Lk - 1, q0 + BR - 1 + delta);
+      const int last_key = min(T.Lk - 1, T.qt * BR + BR - 1 + (T.Lk - T.Lq));
       n_sub = last_key < 0 ? 0 : min(n_sub, last_key / SUB + 1);
     }
+    return n_sub;
+  };
+
+  // A tile's first loads: K stage 0 into buffer 0, and the wave's Q rows
+  // (rows past the end repeat the last row: their results are never stored,
+  // and nothing waits here for the loads to land).
+  auto prefetch = [&](const Tile& T, State& st) __attribute__((always_inline)) {
+    if (tile_subs(T) > 0) dma.issue_asm(T.kbase, kv_stride, 0, T.Lk - 1, lds, lds_base, wave, lane);
+    const int qw0 = T.qt * BR + wave * 64;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int qi = qw0 + t * 32 + m32;
+      const uint16_t* qp =
+          p.q + (size_t)(T.q_start + min(qi, T.Lq - 1)) * q_stride + (size_t)T.h * D + 8 * hh;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+        st.qf[t][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * s));
+    }
+  };
+
+  // The key loop of a tile whose prefetch has been issued.
+  auto body = [&](const Tile& T, State& st) __attribute__((always_inline)) {
+    const int q0 = T.qt * BR;
+    const int delta = T.Lk - T.Lq;  // bottom-right causal offset
+    const int n_sub = tile_subs(T);
     const int n_stage = (n_sub + 1) / 2;
     const int qw0 = q0 + wave * 64;
-    const bool wave_active = qw0 < Lq;
-    const int wave_last_key = CAUSAL ? min(Lk - 1, qw0 + 63 + delta) : Lk - 1;
+    const bool wave_active = qw0 < T.Lq;
+    const int wave_last_key = CAUSAL ? min(T.Lk - 1, qw0 + 63 + delta) : T.Lk - 1;
     // sub-tiles this wave needs (causal: up to its own diagonal)
     const int n_w =
         (wave_active && wave_last_key >= 0) ? min(n_sub, wave_last_key / SUB + 1) : 0;
-
-    if (n_stage > 0) dma.issue_asm(kbase, kv_stride, 0, Lk - 1, lds, lds_base, wave, lane);
-
-    State st;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       st.mc[t] = -INFINITY;
       st.l[t] = 0.f;
-      // rows past the end repeat the last row: their results are never
-      // stored, and nothing waits here for the loads to land
-      const int qi = qw0 + t * 32 + m32;
-      const uint16_t* qp =
-          p.q + (size_t)(q_start + min(qi, Lq - 1)) * q_stride + (size_t)h * D + 8 * hh;
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s)
-        st.qf[t][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * s));
     }
     // Last admissible key of each of the lane's rows minus 4 hh (the lane's key
     // offset inside a sub-tile); sub-tile j masks against row_lim - 32 j.
@@ -580,13 +641,13 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int qi = qw0 + t * 32 + m32;
-      row_lim[t] = (CAUSAL ? min(Lk - 1, qi + delta) : Lk - 1) - 4 * hh;
+      row_lim[t] = (CAUSAL ? min(T.Lk - 1, qi + delta) : T.Lk - 1) - 4 * hh;
     }
     // sub-tile j needs a mask when it crosses the end of the keys or (causal)
     // the diagonal of this wave's first row
     auto edge = [&](int j) {
       const int k0 = j * SUB;
-      return (k0 + SUB > Lk) || (CAUSAL && k0 + SUB - 1 > qw0 + delta);
+      return (k0 + SUB > T.Lk) || (CAUSAL && k0 + SUB - 1 > qw0 + delta);
     };
 
     // S(j) lives in sA (j even) or sB (j odd), P(j) in pA / pB likewise.
@@ -606,10 +667,10 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
       __syncthreads();  // everyone's has; K stage J-1 and V stage J-2 are read
       const int par = J & 1;
       if (J + 1 < n_stage)
-        dma.issue_asm(kbase, kv_stride, (J + 1) * STG, Lk - 1, lds + (par ^ 1) * STG_BYTES,
+        dma.issue_asm(T.kbase, kv_stride, (J + 1) * STG, T.Lk - 1, lds + (par ^ 1) * STG_BYTES,
                       lds_base + (par ^ 1) * STG_BYTES, wave, lane);
       if (J < n_stage)
-        dma.issue_asm(vbase, kv_stride, J * STG, Lk - 1, lds + (2 + par) * STG_BYTES,
+        dma.issue_asm(T.vbase, kv_stride, J * STG, T.Lk - 1, lds + (2 + par) * STG_BYTES,
                       lds_base + (2 + par) * STG_BYTES, wave, lane);
     };
     auto limits = [&](const int j, int (&lim)[NT]) __attribute__((always_inline)) {
@@ -648,11 +709,11 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
       constexpr int n = decltype(nc)::value;
       if constexpr (n < PW) {
         constexpr int KB = decltype(kbuf)::value;
-        const auto src = decltype(dma)::src(kbase, kv_stride, KS * STG, Lk - 1);
+        const auto src = decltype(dma)::src(T.kbase, kv_stride, KS * STG, T.Lk - 1);
         dma.template issue_one<n>(src, kv_row_bytes, lds_base + KB * STG_BYTES, wave);
       } else {
         constexpr int VB = decltype(vbuf)::value;
-        const auto src = decltype(dma)::src(vbase, kv_stride, (KS - 1) * STG, Lk - 1);
+        const auto src = decltype(dma)::src(T.vbase, kv_stride, (KS - 1) * STG, T.Lk - 1);
         dma.template issue_one<n - PW>(src, kv_row_bytes, lds_base + (2 + VB) * STG_BYTES,
                                        wave);
       }
@@ -713,15 +774,16 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
 #pragma clang loop unroll(disable)
     for (; J < n_period; ++J) general_period(J);
 
-    // ---- epilogue: O / l, LSE = ln 2 * (r + log2 l) ----
-    // Each row group's 32 rows go through this wave's 16 KB of the (now
-    // idle) K/V stages, so that every global store writes whole rows: row r
-    // of the group holds its head-dim values in 16-byte chunks XOR-swizzled
-    // by r & 15, which keeps both the writes and the row reads free of bank
-    // conflicts.
-    acc_drain();
-    __syncthreads();  // every wave is done reading the K/V stages
-    char* stg = lds + wave * 16384;
+  };
+
+  // O / l and LSE = ln 2 * (r + log2 l).  Each row group's 32 rows go
+  // through this wave's 16 KB epilogue area, so that every global store
+  // writes whole rows: row r of the group holds its head-dim values in
+  // 16-byte chunks XOR-swizzled by r & 15, which keeps both the writes and
+  // the row reads free of bank conflicts.  Only this wave uses its area.
+  auto epilogue = [&](const Tile& T, const State& st) __attribute__((always_inline)) {
+    const int qw0 = T.qt * BR + wave * 64;
+    char* stg = lds + 4 * STG_BYTES + wave * 16384;
     const bool f32 = p.o_f32 != 0;
     const int row_bytes = f32 ? 4 * D : 2 * D;
 #pragma unroll
@@ -730,7 +792,7 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
       const float lse = lt > 0.f ? (st.mc[t] + __log2f(lt)) * kLn2 : -INFINITY;
       const int qi = qw0 + t * 32 + m32;
-      if (qi < Lq && hh == 0) p.lse[(size_t)(q_start + qi) * p.hq + h] = lse;
+      if (qi < T.Lq && hh == 0) p.lse[(size_t)(T.q_start + qi) * p.hq + T.h] = lse;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         float x[16];
@@ -770,27 +832,33 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
         const u32x4 w =
             *reinterpret_cast<const u32x4*>(stg + r * row_bytes + ((c ^ (r & 15)) << 4));
         const int qr = qw0 + t * 32 + r;
-        if (qr < Lq) {
+        if (qr < T.Lq) {
           char* op = reinterpret_cast<char*>(p.o) +
-                     ((size_t)(q_start + qr) * p.hq + h) * row_bytes + 16 * c;
+                     ((size_t)(T.q_start + qr) * p.hq + T.h) * row_bytes + 16 * c;
           *reinterpret_cast<u32x4*>(op) = w;
         }
       }
     }
-  };  // run_tile
+  };
 
-  if constexpr (PAIR) {
-    // Causal: tile n-1-i (heaviest) then tile i, n counted per sequence, so
-    // every workgroup of a sequence gets about the same work.
-    const int first = (Lq + BR - 1) / BR - 1 - it;
-    if (first < it) return;  // past the middle of a shorter sequence (uniform)
-    run_tile(first);
-    if (it < first) {
-      __syncthreads();  // every wave is done with the first tile's LDS stages
-      run_tile(it);
-    }
-  } else {
-    if (it * BR < Lq) run_tile(it);
+  Tile cur;
+  int k = next_task(0, cur);
+  if (k < 0) return;
+  State st;
+  prefetch(cur, st);
+#pragma clang loop unroll(disable)
+  while (true) {
+    body(cur, st);
+    Tile nxt;
+    const int kn = next_task(k + 1, nxt);
+    acc_drain();
+    __syncthreads();  // every wave is done reading the K/V stages
+    // the next tile's Q goes to st.qf, which the epilogue does not read
+    if (kn >= 0) prefetch(nxt, st);
+    epilogue(cur, st);
+    if (kn < 0) break;
+    cur = nxt;
+    k = kn;
   }
 }
 
@@ -807,10 +875,40 @@ void fwd_wide_kernel(const FwdParams p) {
 template __global__ void fwd_wide_kernel<4, false, false>(const FwdParams);
 template __global__ void fwd_wide_kernel<2, false, false>(const FwdParams);
 
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+// Compute units of the current device (0 if unknown), looked up once.
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = g_cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      return 0;
+    g_cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+}  // namespace
+
 hipError_t launch_fwd_wide(const FwdParams& p, bool causal, hipStream_t stream) {
   if (causal) return hipErrorInvalidValue;  // causal calls run the 32-row kernels
+  // One workgroup fills a compute unit.  A fixed-length batch, whose tiles
+  // all cost the same, runs one workgroup per compute unit, each taking
+  // every (CUs)-th tile, so that a tile's first loads overlap the previous
+  // tile's epilogue.  A multiple of 8 workgroups keeps every tile of a
+  // workgroup on the same XCD as its block index.  Packed sequences keep one
+  // workgroup per tile, which the hardware hands out as compute units free up.
+  int grid = p.total;
+  const int cus = device_cus() & ~7;
+  if (!p.cu_q && cus > 0 && grid > cus) grid = cus;
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(p.total), dim3(p.waves * 64), 0, stream, p);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(p.waves * 64), 0, stream, p);
     return hipGetLastError();
   };
   return p.waves == 4 ? go(fwd_wide_kernel<4, false, false>)
