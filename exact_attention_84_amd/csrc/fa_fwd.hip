@@ -682,8 +682,9 @@ static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
 // workgroups for short or packed sequences).  Causal calls keep the 32-row
 // waves at two waves per SIMD: at the diagonal, where the waves of a
 // workgroup run out of key tiles at different times, the second wave of a
-// SIMD keeps its matrix core busy, and these kernels measured 5-7 % faster
-// on every causal workload.  The 32-row kernels (also head dim 64, the
+// SIMD keeps its matrix core busy.  Against the 64-row kernel with its
+// branch-free tile loads and tile loop, these measured 1-4 % faster on the
+// causal workloads (equal on the long GQA one).  The 32-row kernels (also head dim 64, the
 // score variants and FP8) take 8 waves (256 rows, half the K/V loads per
 // query) for fixed-length batches of at least 2048 queries at head dim 128,
 // else 4.

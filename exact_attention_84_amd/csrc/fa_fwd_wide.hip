@@ -43,6 +43,7 @@ constexpr int NT = 2;                    // 32-row groups per wave
 constexpr int SUB = 32;                  // keys per pipeline sub-step
 constexpr int STG = 64;                  // keys per LDS stage
 constexpr int STG_BYTES = STG * D * 2;   // 16 KB
+constexpr int kEpiBytes = 32 * 256;      // a wave's epilogue area: 32 rows x 256 bytes
 
 // ---------------------------------------------------------------------------
 // O^T accumulators in hard-named AGPRs: block b = 4 t + dt (row group t,
@@ -506,8 +507,9 @@ __device__ __forceinline__ void general_sub(int j, int n_w, State& st,
 template <int NW, bool CAUSAL, bool PAIR>
 __device__ __forceinline__ void wide_body(const FwdParams& p) {
   constexpr int BR = NW * 64;
-  // K stages 0 and 1, V stages 0 and 1, then one 16 KB epilogue area per wave
-  __shared__ __attribute__((aligned(1024))) char lds[4 * STG_BYTES + NW * 16384];
+  // K stages 0 and 1, V stages 0 and 1, then one epilogue area per wave
+  // (80 KB in all for two waves, so that two such workgroups share a CU)
+  __shared__ __attribute__((aligned(1024))) char lds[4 * STG_BYTES + NW * kEpiBytes];
   const uint32_t lds_base = lds_address(lds);
 
   const int tid = threadIdx.x;
@@ -776,16 +778,32 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
 
   };
 
-  // O / l and LSE = ln 2 * (r + log2 l).  Each row group's 32 rows go
-  // through this wave's 16 KB epilogue area, so that every global store
-  // writes whole rows: row r of the group holds its head-dim values in
-  // 16-byte chunks XOR-swizzled by r & 15, which keeps both the writes and
-  // the row reads free of bank conflicts.  Only this wave uses its area.
+  // O / l and LSE = ln 2 * (r + log2 l).  The output goes out in pieces of
+  // 32 rows x 256 bytes (a row group's whole bf16 rows, or half of its fp32
+  // rows) through this wave's 8 KB epilogue area, so that every global store
+  // writes 16-byte chunks of one contiguous 256-byte run: row r of a piece
+  // holds its 16 chunks XOR-swizzled by r & 15, which keeps both the writes
+  // and the row reads free of bank conflicts.  Only this wave uses its area.
   auto epilogue = [&](const Tile& T, const State& st) __attribute__((always_inline)) {
     const int qw0 = T.qt * BR + wave * 64;
-    char* stg = lds + 4 * STG_BYTES + wave * 16384;
+    char* stg = lds + 4 * STG_BYTES + wave * kEpiBytes;
     const bool f32 = p.o_f32 != 0;
-    const int row_bytes = f32 ? 4 * D : 2 * D;
+    const size_t o_row = (size_t)p.hq * (f32 ? 4 * D : 2 * D);  // bytes per token
+    // rows back out, 16 bytes per lane, 4 rows per wave instruction
+    auto store_piece = [&](const int t, const int piece) __attribute__((always_inline)) {
+      const int c = lane & 15;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        const u32x4 w = *reinterpret_cast<const u32x4*>(stg + r * 256 + ((c ^ (r & 15)) << 4));
+        const int qr = qw0 + t * 32 + r;
+        if (qr < T.Lq) {
+          char* op = reinterpret_cast<char*>(p.o) + (size_t)(T.q_start + qr) * o_row +
+                     (size_t)T.h * (f32 ? 4 * D : 2 * D) + piece * 256 + 16 * c;
+          *reinterpret_cast<u32x4*>(op) = w;
+        }
+      }
+    };
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const float lt = halfwave_sum(st.l[t]);
@@ -810,10 +828,11 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           if (f32) {
-            const int c = dt * 8 + 2 * g + hh;  // 16-byte chunk of the 512-byte row
+            // fp32 pieces hold head-dim blocks dt = 2 piece, 2 piece + 1
+            const int c = (dt & 1) * 8 + 2 * g + hh;
             const f32x4 w = {x[4 * g] * inv, x[4 * g + 1] * inv, x[4 * g + 2] * inv,
                              x[4 * g + 3] * inv};
-            *reinterpret_cast<f32x4*>(stg + m32 * 512 + ((c ^ (m32 & 15)) << 4)) = w;
+            *reinterpret_cast<f32x4*>(stg + m32 * 256 + ((c ^ (m32 & 15)) << 4)) = w;
           } else {
             const int c = dt * 4 + g;  // 16-byte chunk of the 256-byte row, half hh
             const u32x2 w = {pack_bf16x2(x[4 * g] * inv, x[4 * g + 1] * inv),
@@ -821,23 +840,9 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
             *reinterpret_cast<u32x2*>(stg + m32 * 256 + ((c ^ (m32 & 15)) << 4) + 8 * hh) = w;
           }
         }
+        if (f32 && (dt & 1)) store_piece(t, dt >> 1);
       }
-      // rows back out, 16 bytes per lane: 64 / (row_bytes / 16) rows per
-      // wave instruction, each row one contiguous run in memory
-      const int cpr = row_bytes / 16;  // chunks per row
-      const int c = lane % cpr;
-#pragma unroll
-      for (int i = 0; i < (f32 ? 16 : 8); ++i) {
-        const int r = i * (f32 ? 2 : 4) + lane / cpr;
-        const u32x4 w =
-            *reinterpret_cast<const u32x4*>(stg + r * row_bytes + ((c ^ (r & 15)) << 4));
-        const int qr = qw0 + t * 32 + r;
-        if (qr < T.Lq) {
-          char* op = reinterpret_cast<char*>(p.o) +
-                     ((size_t)(T.q_start + qr) * p.hq + T.h) * row_bytes + 16 * c;
-          *reinterpret_cast<u32x4*>(op) = w;
-        }
-      }
+      if (!f32) store_piece(t, 0);
     }
   };
 
@@ -870,10 +875,10 @@ void fwd_wide_kernel(const FwdParams p) {
   wide::wide_body<NW, CAUSAL, PAIR>(p);
 }
 
-// Only the non-causal instances are built: fwd_plan sends causal calls to
-// the 32-row-wave kernels.
 template __global__ void fwd_wide_kernel<4, false, false>(const FwdParams);
 template __global__ void fwd_wide_kernel<2, false, false>(const FwdParams);
+// Causal calls run the 32-row kernels of fa_fwd.hip: with the diagonal at
+// 64-row granularity these measured 1-4 % slower on the causal workloads.
 
 namespace {
 
@@ -897,7 +902,7 @@ int device_cus() {
 }  // namespace
 
 hipError_t launch_fwd_wide(const FwdParams& p, bool causal, hipStream_t stream) {
-  if (causal) return hipErrorInvalidValue;  // causal calls run the 32-row kernels
+  if (causal) return hipErrorInvalidValue;
   // One workgroup fills a compute unit.  A fixed-length batch, whose tiles
   // all cost the same, runs one workgroup per compute unit, each taking
   // every (CUs)-th tile, so that a tile's first loads overlap the previous
