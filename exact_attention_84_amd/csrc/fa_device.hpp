@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "fa_layout.hpp"
 
 namespace fa {
@@ -227,6 +229,17 @@ __device__ __forceinline__ void dma16(const void* g, char* lds_dst) {
 __device__ __forceinline__ void dma16_s(uint32_t off, const void* base, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(off), "s"(base), "s"(lds_addr) : "memory", "m0");
+}
+
+// Calls f(integral_constant<int, i>) for i = 0 .. N-1, every index a
+// compile-time constant.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
 }
 
 // A pointer that is the same in every lane, moved to scalar registers.

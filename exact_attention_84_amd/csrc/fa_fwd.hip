@@ -459,14 +459,29 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, int win_left, int w
   for (int t = 0; t < NT; ++t) row_rel[t] = qw0 + t * 32 + m32 + delta - 4 * hh;
   // Step j: K_j and V_{j-1} are in LDS; K_{j+1} and V_j start streaming into
   // the stages that K_{j-1} and V_{j-2} used.
+  // The loads are asm, issued with no branch per instruction (the tile's rows
+  // clamped to the last key); wait_dma and the barrier order them.
+  constexpr int PW = decltype(dma)::PER_WAVE;
+  const uint32_t kv_row_bytes = 2u * (uint32_t)kv_stride;
   auto stage = [&](int j) {
     wait_dma();       // this wave's share of K_j and V_{j-1} has landed
     __syncthreads();  // everyone's has, and everyone is done with K_{j-1}, V_{j-2}
-    if (j + 1 < n_kt)
-      dma.issue(kbase, kv_stride, (kt0 + j + 1) * BC, Lk - 1, (j & 1) ? k_lds0 : k_lds1, wave,
-                lane);
-    if (j < n_kt)
-      dma.issue(vbase, kv_stride, (kt0 + j) * BC, Lk - 1, (j & 1) ? v_lds1 : v_lds0, wave, lane);
+    if (j + 1 < n_kt) {
+      const auto src = decltype(dma)::src(kbase, kv_stride, (kt0 + j + 1) * BC, Lk - 1);
+      const uint32_t at = lds_address((j & 1) ? k_lds0 : k_lds1);
+      auto one = [&](auto nc) {
+        dma.template issue_one<decltype(nc)::value>(src, kv_row_bytes, at, wave);
+      };
+      static_for<PW>(one);
+    }
+    if (j < n_kt) {
+      const auto src = decltype(dma)::src(vbase, kv_stride, (kt0 + j) * BC, Lk - 1);
+      const uint32_t at = lds_address((j & 1) ? v_lds1 : v_lds0);
+      auto one = [&](auto nc) {
+        dma.template issue_one<decltype(nc)::value>(src, kv_row_bytes, at, wave);
+      };
+      static_for<PW>(one);
+    }
   };
 
   // The O rescale of tile j (alpha_j, when some row moved its reference) must
@@ -537,6 +552,10 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, int win_left, int w
   };
   if (wn > 1) {
     general_step(0);  // softmax of S_0 -> p_a
+    // the Q loads are known complete from here on: the compiler then puts no
+    // waits for them inside the loop, where the counter also counts the asm
+    // tile loads (step 1 waits for those anyway)
+    vm_drain();
     j = 1;
 #pragma clang loop unroll(disable)
     while (j < wn) {

@@ -187,16 +187,6 @@ __device__ __forceinline__ void pv_pair_dt(int dt, bf16x8 v, bf16x8 p0, bf16x8 p
 // ---------------------------------------------------------------------------
 // Per-wave state and one 32-key sub-tile's pieces.
 // ---------------------------------------------------------------------------
-// Calls f(integral_constant<int, i>) for i = 0 .. N-1, every index a
-// compile-time constant.
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_seq(F& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F& f) {
-  static_for_seq(f, std::make_integer_sequence<int, N>{});
-}
 
 // dst = src through a move whose output is tied to dst's register.  Used
 // where a rare branch recomputes values that the common path leaves in
