@@ -272,10 +272,23 @@ void bwd_dq_kernel(const BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m32 = lane & 31, hh = lane >> 5;
 
-  const int total = p.batch * p.hq * p.n_qtiles;
-  const int item = xcd_remap(blockIdx.x, total, p.group * p.n_qtiles);
-  const int it = item % p.n_qtiles;
-  int rest = item / p.n_qtiles;
+  // Work item: (sequence b, kv head, query head in group) and query tile qt.
+  // Causal tiles cost in proportion to qt + 1, so blocks take them heaviest
+  // first over all heads (block w: tile rank w / heads, head w % heads); the
+  // hardware hands blocks out in order as compute units free up, and the
+  // light tiles fill the gaps the heavy ones leave.  Either way the heads of
+  // one kv group, which read the same K and V, share an XCD.
+  const int nh = p.batch * p.hq;
+  int it, rest;
+  if (CAUSAL) {
+    const int u = blockIdx.x % nh;
+    it = blockIdx.x / nh;
+    rest = xcd_remap(u, nh, p.group);
+  } else {
+    const int item = xcd_remap(blockIdx.x, nh * p.n_qtiles, p.group * p.n_qtiles);
+    it = item % p.n_qtiles;
+    rest = item / p.n_qtiles;
+  }
   const int hg = rest % p.group;
   rest /= p.group;
   const int kvh = rest % p.hkv;
@@ -294,7 +307,7 @@ void bwd_dq_kernel(const BwdParams p) {
     k_start = b * p.seqlen_k;
     Lk = p.seqlen_k;
   }
-  const int qt = CAUSAL ? p.n_qtiles - 1 - it : it;  // causal: heaviest tiles first
+  const int qt = CAUSAL ? p.n_qtiles - 1 - it : it;
   const int q0 = qt * BR;
   if (q0 >= Lq) return;  // packed sequence shorter than this tile (uniform)
 
@@ -411,10 +424,20 @@ void bwd_dkdv_kernel(const BwdParams p) {
   const bool dp_role = wave >= 4;  // uniform per wave
   const int hh = lane >> 5, m32 = lane & 31;
 
-  const int total = p.batch * p.hkv * p.n_kblocks;
-  const int item = xcd_remap(blockIdx.x, total, p.n_kblocks);
-  const int kblk = item % p.n_kblocks;
-  const int rest = item / p.n_kblocks;
+  // Work item: (sequence b, kv head) and key block kblk.  A causal block
+  // costs in proportion to the query tiles below its diagonal, most for
+  // block 0, so blocks take them heaviest first over all heads (block w: key
+  // block w / heads, head w % heads), as the dQ kernel does.
+  const int nkv = p.batch * p.hkv;
+  int kblk, rest;
+  if (CAUSAL) {
+    kblk = blockIdx.x / nkv;
+    rest = blockIdx.x % nkv;
+  } else {
+    const int item = xcd_remap(blockIdx.x, nkv * p.n_kblocks, p.n_kblocks);
+    kblk = item % p.n_kblocks;
+    rest = item / p.n_kblocks;
+  }
   const int kvh = rest % p.hkv;
   const int b = rest / p.hkv;
 
