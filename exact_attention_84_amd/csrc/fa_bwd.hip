@@ -351,11 +351,26 @@ void bwd_dq_kernel(const BwdParams p) {
   dma.init(kv_stride, wave, lane);
   LdsRead<D> rd;
   rd.init(lane);
-  if (n_kt > 0) {
-    dma.issue(kbase, kv_stride, 0, Lk - 1, k_lds0, wave, lane);
-    dma.issue(vbase, kv_stride, 0, Lk - 1, v_lds0, wave, lane);
-  }
+  // K and V tile j into stage s, as asm loads with no branch per instruction
+  // (rows clamped to the last key); wait_dma and the barrier order them
+  constexpr int PW = decltype(dma)::PER_WAVE;
+  const uint32_t kv_row_bytes = 2u * (uint32_t)kv_stride;
+  auto load_tiles = [&](const int j, char* k_dst, char* v_dst) {
+    const auto ks = decltype(dma)::src(kbase, kv_stride, j * BC, Lk - 1);
+    const auto vs = decltype(dma)::src(vbase, kv_stride, j * BC, Lk - 1);
+    const uint32_t ka = lds_address(k_dst), va = lds_address(v_dst);
+    auto one = [&](auto nc) {
+      dma.template issue_one<decltype(nc)::value>(ks, kv_row_bytes, ka, wave);
+      dma.template issue_one<decltype(nc)::value>(vs, kv_row_bytes, va, wave);
+    };
+    static_for<PW>(one);
+  };
+  if (n_kt > 0) load_tiles(0, k_lds0, v_lds0);
   const int wave_last_key = CAUSAL ? min(Lk - 1, qw0 + 31 + delta) : Lk - 1;
+  // Q, dO and the row statistics are known loaded from here on: the
+  // compiler then places no waits for them inside the loop, where the
+  // counter also counts the asm tile loads
+  vm_drain();
 
 #pragma clang loop unroll(disable)
   for (int j = 0; j < n_kt; ++j) {
@@ -363,10 +378,7 @@ void bwd_dq_kernel(const BwdParams p) {
     const char* vc = (j & 1) ? v_lds1 : v_lds0;
     wait_dma();
     __syncthreads();  // K_j, V_j have landed; everyone is done with the other stage
-    if (j + 1 < n_kt) {
-      dma.issue(kbase, kv_stride, (j + 1) * BC, Lk - 1, (j & 1) ? k_lds0 : k_lds1, wave, lane);
-      dma.issue(vbase, kv_stride, (j + 1) * BC, Lk - 1, (j & 1) ? v_lds0 : v_lds1, wave, lane);
-    }
+    if (j + 1 < n_kt) load_tiles(j + 1, (j & 1) ? k_lds0 : k_lds1, (j & 1) ? v_lds0 : v_lds1);
     if (qw0 >= Lq) continue;  // this wave has no rows (uniform)
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {

@@ -47,31 +47,32 @@ template <int NW, bool V_TILE>
 struct Dma8 {
   static constexpr int PER_WAVE = 8 / NW;
   static_assert(8 % NW == 0, "tile instructions must split evenly over the waves");
-  int off[PER_WAVE];
+  int row[PER_WAVE];         // the lane's tile row in each instruction
+  uint32_t cbytes[PER_WAVE];  // byte offset of its 16-byte chunk in that row
 
-  __device__ __forceinline__ void init(int row_stride, int wave, int lane) {
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
     for (int n = 0; n < PER_WAVE; ++n) {
       const int inst = wave + n * NW;
-      off[n] = dma8_row(inst, lane) * row_stride + (dma8_chunk(inst, lane, V_TILE) << 4);
+      row[n] = dma8_row(inst, lane);
+      cbytes[n] = (uint32_t)dma8_chunk(inst, lane, V_TILE) << 4;
     }
   }
+  // With no branch: the scalar base is the tile's first row (row klast when
+  // the whole tile lies past it) and each lane's 32-bit offset is its row,
+  // clamped to klast, times the pitch plus its chunk, so every address stays
+  // inside rows 0..klast.  row_stride is below 2^24.
   __device__ __forceinline__ void issue(const uint8_t* __restrict__ base, int row_stride, int k0,
-                                        int klast, char* lds, int wave, int lane) const {
-    const uint8_t* tile = base + (size_t)k0 * row_stride;
-    if (k0 + kBC8 - 1 <= klast) {
+                                        int klast, char* lds, int wave) const {
+    const int k = min(k0, klast);
+    const uint8_t* tile = base + (size_t)k * row_stride;
+    const int lim = klast - k;
+    const uint32_t at = lds_address(lds);
 #pragma unroll
-      for (int n = 0; n < PER_WAVE; ++n)
-        dma16(tile + off[n], lds + (wave + n * NW) * 1024);
-    } else {
-#pragma unroll
-      for (int n = 0; n < PER_WAVE; ++n) {
-        const int inst = wave + n * NW;
-        const int src = min(k0 + dma8_row(inst, lane), klast);
-        const uint8_t* g =
-            base + (size_t)src * row_stride + (dma8_chunk(inst, lane, V_TILE) << 4);
-        dma16(g, lds + inst * 1024);
-      }
+    for (int n = 0; n < PER_WAVE; ++n) {
+      const uint32_t r = (uint32_t)min(row[n], lim);
+      dma16_s(__umul24(r, (uint32_t)row_stride) + cbytes[n], tile,
+              at + (wave + n * NW) * 1024);
     }
   }
 };
@@ -301,15 +302,15 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdParams& p, float v_descale
 
     Dma8<NW, false> dk;
     Dma8<NW, true> dv;
-    dk.init(kv_stride, wave, lane);
-    dv.init(kv_stride, wave, lane);
+    dk.init(wave, lane);
+    dv.init(wave, lane);
     Rd8 rd;
     rd.init(lane);
     // K_0, then K_1 and V_0 (step j waits for K_j and V_{j-1}, issued a step
     // before the loads it may leave in flight)
-    if (n_kt > 0) dk.issue(kbase, kv_stride, 0, Lk - 1, k_lds, wave, lane);
-    if (n_kt > 1) dk.issue(kbase, kv_stride, kBC8, Lk - 1, k_lds + kTile8, wave, lane);
-    if (n_kt > 0) dv.issue(vbase, kv_stride, 0, Lk - 1, v_lds, wave, lane);
+    if (n_kt > 0) dk.issue(kbase, kv_stride, 0, Lk - 1, k_lds, wave);
+    if (n_kt > 1) dk.issue(kbase, kv_stride, kBC8, Lk - 1, k_lds + kTile8, wave);
+    if (n_kt > 0) dv.issue(vbase, kv_stride, 0, Lk - 1, v_lds, wave);
 
     State8 st;
     st.mc = -INFINITY;
@@ -362,9 +363,9 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdParams& p, float v_descale
       wait_tiles_upto<PER>((j + 1 < n_kt ? 1 : 0) + (j < n_kt ? 1 : 0));
       __syncthreads();
       if (j + 2 < n_kt)
-        dk.issue(kbase, kv_stride, (j + 2) * kBC8, Lk - 1, k_lds + s2 * kTile8, wave, lane);
+        dk.issue(kbase, kv_stride, (j + 2) * kBC8, Lk - 1, k_lds + s2 * kTile8, wave);
       if (j + 1 < n_kt)
-        dv.issue(vbase, kv_stride, (j + 1) * kBC8, Lk - 1, v_lds + s1 * kTile8, wave, lane);
+        dv.issue(vbase, kv_stride, (j + 1) * kBC8, Lk - 1, v_lds + s1 * kTile8, wave);
       k_cur = k_lds + s0 * kTile8;
       v_prev = v_lds + s2 * kTile8;
       s0 = s1;
