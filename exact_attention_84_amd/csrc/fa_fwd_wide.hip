@@ -893,15 +893,16 @@ int device_cus() {
 
 hipError_t launch_fwd_wide(const FwdParams& p, bool causal, hipStream_t stream) {
   if (causal) return hipErrorInvalidValue;
-  // One workgroup fills a compute unit.  A fixed-length batch, whose tiles
-  // all cost the same, runs one workgroup per compute unit, each taking
-  // every (CUs)-th tile, so that a tile's first loads overlap the previous
+  // Each wave takes a whole SIMD, so 4 / waves workgroups fill a compute
+  // unit.  A fixed-length batch, whose tiles all cost the same, launches
+  // just enough workgroups to fill every compute unit once, each taking
+  // every (grid)-th tile, so that a tile's first loads overlap the previous
   // tile's epilogue.  A multiple of 8 workgroups keeps every tile of a
   // workgroup on the same XCD as its block index.  Packed sequences keep one
   // workgroup per tile, which the hardware hands out as compute units free up.
   int grid = p.total;
-  const int cus = device_cus() & ~7;
-  if (!p.cu_q && cus > 0 && grid > cus) grid = cus;
+  const int slots = (device_cus() & ~7) * (4 / p.waves);
+  if (!p.cu_q && slots > 0 && grid > slots) grid = slots;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(p.waves * 64), 0, stream, p);
     return hipGetLastError();
