@@ -187,6 +187,37 @@ def test_full_workload_sampled_rows(fa, wid, causal):
         assert np.isfinite(og).all() and np.isfinite(lg).all()
 
 
+@pytest.mark.parametrize("shape", [(24, 8, 640), (6, 16, 2048)])
+def test_tile_loop_sampled_rows(fa, shape):
+    """Fixed-length non-causal batches with more query tiles than the chip
+    holds workgroups at once, so that workgroups run several tiles in turn:
+    640 queries take 128-row (2-wave) workgroups, 2048 take 256-row ones.
+    Rows are sampled from every query tile position."""
+    import torch
+    bsz, hq, n = shape
+    br = 128 if n < 1024 else 256
+    slots = torch.cuda.get_device_properties(0).multi_processor_count * (256 // br)
+    tiles = bsz * hq * (n // br)
+    assert tiles > slots, f"{tiles} tiles fit in one round of {slots} workgroups"
+    say("tile loop", shape, tiles, "tiles", slots, "slots")
+    q = W.normal_bf16(7, 240, 0, (bsz, n, hq, 128))
+    k = W.normal_bf16(7, 240, 1, (bsz, n, hq, 128))
+    v = W.normal_bf16(7, 240, 2, (bsz, n, hq, 128))
+    scale = 1 / np.sqrt(128)
+    o, lse = fa.attention(dev_bf16(q), dev_bf16(k), dev_bf16(v), causal=False, scale=scale,
+                          out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = [(int(rng.integers(bsz)), t * br + int(rng.integers(br)), int(rng.integers(hq)))
+            for t in range(n // br) for _ in range(6)]
+    rows += [(bsz - 1, n - 1, hq - 1), (0, 0, 0)]
+    orf, lrf = oracle.attention_rows(q, k, v, rows, scale, False)
+    og, lg = host(o), host(lse)
+    check_o(np.stack([og[b, i, h] for (b, i, h) in rows]), orf, False, "tile loop")
+    check_lse(np.array([lg[b, i, h] for (b, i, h) in rows]), lrf, "tile loop")
+    assert np.isfinite(og).all() and np.isfinite(lg).all()
+
+
 def test_full_varlen_workload_sampled_rows(fa):
     import torch
     w = W.WORKLOADS[4]
