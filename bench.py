@@ -5,11 +5,14 @@
 
 One step is one pass of the hot path over the batched-MHA workload
 (B=4, H=16, N=2048, d=128, bf16, scale 1/sqrt(128)) in both of its modes,
-non-causal then causal.  ``value`` is the step's algorithmic TFLOP/s
+non-causal and causal.  ``value`` is the step's algorithmic TFLOP/s
 (4*B*H*Nq*Nk*d, halved for the causal pass) with inputs already resident in
-device memory.  ``roofline`` reports the dominant kernel (the non-causal
-forward) against the MI355X dense bf16 MFMA peak, timed with HIP events on the
-launch stream.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded
+device memory.  The timed region issues the K steps' non-causal launches
+back to back, then their causal launches, with a HIP event on the launch
+stream at its start, between the two runs and at its end: the two averages
+are the kernels' launch-to-launch times, with no event between launches of a
+run.  ``roofline`` reports the dominant kernel (the non-causal forward)
+against the MI355X dense bf16 MFMA peak.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded
 sample of the same workload.  ``other_workloads`` adds the long causal GQA,
 varlen and split-KV decode workloads (TFLOP/s, or GB/s for decode).
 
@@ -185,38 +188,6 @@ def write_traffic(fetch_dir: str, write_dir: str) -> dict:
 def to_dev(bits):
     import torch
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
-
-
-class LaunchTimer:
-    """HIP-event timing of individual launches on torch's current stream (the
-    stream the library launches on).  One event is recorded after each launch
-    (and one before the first), so a launch's time runs from the end of the
-    previous launch to its own end: back-to-back launches are timed with one
-    event between them rather than a pair around each, which would add an
-    idle gap per launch."""
-
-    def __init__(self):
-        self.events = []
-        self.names = []
-
-    def run(self, name, fn):
-        import torch
-        if not self.events:
-            self.events.append(torch.cuda.Event(enable_timing=True))
-            self.events[0].record()
-        fn()
-        e = torch.cuda.Event(enable_timing=True)
-        e.record()
-        self.events.append(e)
-        self.names.append(name)
-
-    def times_ms(self, name):
-        ev = self.events
-        return [ev[i].elapsed_time(ev[i + 1]) for i, n in enumerate(self.names) if n == name]
-
-    def avg_ms(self, name):
-        t = self.times_ms(name)
-        return sum(t) / max(1, len(t))
 
 
 def time_calls(fn, steps, warmup):
@@ -674,34 +645,32 @@ def main():
     fl_nc = W.flops(w, causal=False)
     fl_c = W.flops(w, causal=True)
 
-    timer = LaunchTimer()
+    def noncausal():
+        fa.attention(q, k, v, causal=False, scale=w.scale, out=o_nc, lse=lse_nc)
 
-    def step(t=None):
-        if t is None:
-            fa.attention(q, k, v, causal=False, scale=w.scale, out=o_nc, lse=lse_nc)
-            fa.attention(q, k, v, causal=True, scale=w.scale, out=o_c, lse=lse_c)
-        else:
-            t.run("noncausal", lambda: fa.attention(q, k, v, causal=False, scale=w.scale,
-                                                    out=o_nc, lse=lse_nc))
-            t.run("causal", lambda: fa.attention(q, k, v, causal=True, scale=w.scale,
-                                                 out=o_c, lse=lse_c))
+    def causal():
+        fa.attention(q, k, v, causal=True, scale=w.scale, out=o_c, lse=lse_c)
 
     for _ in range(a.warmup):
-        step()
+        noncausal()
+        causal()
     torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     wall0 = time.perf_counter()
-    t0.record()
+    ev[0].record()
     for _ in range(a.steps):
-        step(timer)
-    t1.record()
+        noncausal()
+    ev[1].record()
+    for _ in range(a.steps):
+        causal()
+    ev[2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step = t0.elapsed_time(t1) / a.steps
+    ms_step = ev[0].elapsed_time(ev[2]) / a.steps
+    ms_nc = ev[0].elapsed_time(ev[1]) / a.steps
+    ms_c = ev[1].elapsed_time(ev[2]) / a.steps
     assert torch.isfinite(o_nc.float()).all() and torch.isfinite(o_c.float()).all()
     value = (fl_nc + fl_c) / (ms_step * 1e-3) / 1e12
-    ms_nc, ms_c = timer.avg_ms("noncausal"), timer.avg_ms("causal")
-    t_nc = sorted(timer.times_ms("noncausal"))
     flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
     ms_cold = cold_launches(lambda: fa.attention(q, k, v, causal=False, scale=w.scale, out=o_nc,
                                                  lse=lse_nc), 20, flush)
@@ -739,9 +708,7 @@ def main():
                      "flop_per_launch": fl_nc},
         "causal_launch": {"avg_launch_ms": round(ms_c, 5),
                           "tflops": round(fl_c / (ms_c * 1e-3) / 1e12, 2)},
-        "noncausal_launch_ms": {"median": round(t_nc[len(t_nc) // 2], 5),
-                                "min": round(t_nc[0], 5),
-                                "cold_cache_avg": round(ms_cold, 5),
+        "noncausal_launch_ms": {"cold_cache_avg": round(ms_cold, 5),
                                 "cold_cache_tflops": round(fl_nc / (ms_cold * 1e-3) / 1e12, 2)},
     }
     del o_nc, o_c, lse_nc, lse_c
