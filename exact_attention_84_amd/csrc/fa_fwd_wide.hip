@@ -371,7 +371,10 @@ __device__ __forceinline__ void steady_sub(State& st, const char* __restrict__ k
   u32x4 pw[NT][2];
   float x[NE], pe[NE];
   // fragments: K for score k-step m (slots 4m, 4m+2), V for P V step m (slots
-  // 4m+1, 4m+3), each read one k-step ahead
+  // 4m+1, 4m+3), each read one k-step ahead.  A slot issues its matrix
+  // instruction, then its operand reads, then the softmax work: reads issued
+  // behind the ALU instructions of a slot cost the wave several cycles each
+  // more than reads issued right after the matrix instruction.
   bf16x8 kf[2], vf[2];
   kf[0] = kf0;
   vf[0] = vf0;
@@ -380,16 +383,19 @@ __device__ __forceinline__ void steady_sub(State& st, const char* __restrict__ k
     constexpr int i = decltype(ic)::value;
     constexpr int m = i >> 2;
     if constexpr ((i & 3) == 0) {
+      sn[0] = mfma_32x32x16(kf[m & 1], st.qf[0][m], m == 0 ? f32x16{} : sn[0]);
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (m + 1 < 8) kf[(m + 1) & 1] = rd.k(k_st, KT, m + 1);
       if constexpr (m == 7 && KT == 0) kf0 = rd.k(k_st, 1, 0);
-      sn[0] = mfma_32x32x16(kf[m & 1], st.qf[0][m], m == 0 ? f32x16{} : sn[0]);
     } else if constexpr ((i & 3) == 1) {
+      Acc<m & 3>::mfma(vf[m & 1], pp[0][m >> 2]);
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (m + 1 < 8) vf[(m + 1) & 1] = rd.v(v_st, KT, (m + 1) >> 2, (m + 1) & 3);
       if constexpr (m == 7 && KT == 0) vf0 = rd.v(v_st, 1, 0, 0);
-      Acc<m & 3>::mfma(vf[m & 1], pp[0][m >> 2]);
       // slot 29: every operand read of this period's stages has been waited
       // for (the last V fragment before this product, the last K fragment
-      // before slot 28's), so the next period's loads may overwrite them
+      // before slot 28's) and none is issued here, so the next period's
+      // loads may overwrite them
       if constexpr (i == 29 && KT == 1) {
         if (do_stage) stage(kf0, vf0);
       }
