@@ -784,20 +784,48 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
     const int qw0 = T.qt * BR + wave * 64;
     char* stg = lds + 4 * STG_BYTES + wave * kEpiBytes;
     const bool f32 = p.o_f32 != 0;
-    const size_t o_row = (size_t)p.hq * (f32 ? 4 * D : 2 * D);  // bytes per token
+    const size_t esz = f32 ? 4 : 2;                // bytes per output value
+    const size_t o_row = (size_t)p.hq * D * esz;  // bytes per token
+    const int c = lane & 15;
+    // The lane stores row 4 i + (lane >> 4) of a piece at o_lane + (32 t +
+    // 4 i) o_row + 256 piece: one per-lane product per tile, and a constant
+    // multiple of the uniform row pitch per store.
+    char* const o_lane = reinterpret_cast<char*>(p.o) +
+                         (size_t)(T.q_start + qw0 + (lane >> 4)) * o_row +
+                         (size_t)T.h * D * esz + 16 * c;
+    // Rows that exist from the lane's first row on.  Every row of a wave whose
+    // 64 rows are all inside the sequence exists, and its stores test nothing.
+    const int rows_left = T.Lq - qw0 - (lane >> 4);
+    const bool full = qw0 + 64 <= T.Lq;
     // rows back out, 16 bytes per lane, 4 rows per wave instruction
     auto store_piece = [&](const int t, const int piece) __attribute__((always_inline)) {
-      const int c = lane & 15;
+      u32x4 w[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = 4 * i + (lane >> 4);
-        const u32x4 w = *reinterpret_cast<const u32x4*>(stg + r * 256 + ((c ^ (r & 15)) << 4));
-        const int qr = qw0 + t * 32 + r;
-        if (qr < T.Lq) {
-          char* op = reinterpret_cast<char*>(p.o) + (size_t)(T.q_start + qr) * o_row +
-                     (size_t)T.h * (f32 ? 4 * D : 2 * D) + piece * 256 + 16 * c;
-          *reinterpret_cast<u32x4*>(op) = w;
-        }
+        w[i] = *reinterpret_cast<const u32x4*>(stg + r * 256 + ((c ^ (r & 15)) << 4));
+      }
+      char* const op = o_lane + (size_t)(32 * t) * o_row + 256 * piece;
+      if (full) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(op + (size_t)(4 * i) * o_row) = w[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (32 * t + 4 * i < rows_left)
+            *reinterpret_cast<u32x4*>(op + (size_t)(4 * i) * o_row) = w[i];
+      }
+    };
+    auto read_block = [&](const int b, float (&x)[16]) __attribute__((always_inline)) {
+      switch (b) {
+        case 0: Acc<0>::read(x); break;
+        case 1: Acc<1>::read(x); break;
+        case 2: Acc<2>::read(x); break;
+        case 3: Acc<3>::read(x); break;
+        case 4: Acc<4>::read(x); break;
+        case 5: Acc<5>::read(x); break;
+        case 6: Acc<6>::read(x); break;
+        default: Acc<7>::read(x); break;
       }
     };
 #pragma unroll
@@ -807,38 +835,38 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
       const float lse = lt > 0.f ? (st.mc[t] + __log2f(lt)) * kLn2 : -INFINITY;
       const int qi = qw0 + t * 32 + m32;
       if (qi < T.Lq && hh == 0) p.lse[(size_t)(T.q_start + qi) * p.hq + T.h] = lse;
+      // the lane holds head-dim dt*32 + 8g + 4hh + 0..3 of row m32 in block
+      // 4t + dt, values 4g .. 4g+3
+      if (f32) {
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        float x[16];
-        switch (4 * t + dt) {
-          case 0: Acc<0>::read(x); break;
-          case 1: Acc<1>::read(x); break;
-          case 2: Acc<2>::read(x); break;
-          case 3: Acc<3>::read(x); break;
-          case 4: Acc<4>::read(x); break;
-          case 5: Acc<5>::read(x); break;
-          case 6: Acc<6>::read(x); break;
-          default: Acc<7>::read(x); break;
-        }
-        // the lane's values of head-dim dt*32 + 8g + 4hh + 0..3, row m32
+        for (int dt = 0; dt < D / 32; ++dt) {
+          float x[16];
+          read_block(4 * t + dt, x);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          if (f32) {
+          for (int g = 0; g < 4; ++g) {
             // fp32 pieces hold head-dim blocks dt = 2 piece, 2 piece + 1
-            const int c = (dt & 1) * 8 + 2 * g + hh;
+            const int ch = (dt & 1) * 8 + 2 * g + hh;
             const f32x4 w = {x[4 * g] * inv, x[4 * g + 1] * inv, x[4 * g + 2] * inv,
                              x[4 * g + 3] * inv};
-            *reinterpret_cast<f32x4*>(stg + m32 * 256 + ((c ^ (m32 & 15)) << 4)) = w;
-          } else {
-            const int c = dt * 4 + g;  // 16-byte chunk of the 256-byte row, half hh
+            *reinterpret_cast<f32x4*>(stg + m32 * 256 + ((ch ^ (m32 & 15)) << 4)) = w;
+          }
+          if (dt & 1) store_piece(t, dt >> 1);
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          float x[16];
+          read_block(4 * t + dt, x);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int ch = dt * 4 + g;  // 16-byte chunk of the 256-byte row, half hh
             const u32x2 w = {pack_bf16x2(x[4 * g] * inv, x[4 * g + 1] * inv),
                              pack_bf16x2(x[4 * g + 2] * inv, x[4 * g + 3] * inv)};
-            *reinterpret_cast<u32x2*>(stg + m32 * 256 + ((c ^ (m32 & 15)) << 4) + 8 * hh) = w;
+            *reinterpret_cast<u32x2*>(stg + m32 * 256 + ((ch ^ (m32 & 15)) << 4) + 8 * hh) = w;
           }
         }
-        if (f32 && (dt & 1)) store_piece(t, dt >> 1);
+        store_piece(t, 0);
       }
-      if (!f32) store_piece(t, 0);
     }
   };
 
