@@ -231,6 +231,15 @@ __device__ __forceinline__ void dma16_s(uint32_t off, const void* base, uint32_t
                :: "v"(off), "s"(base), "s"(lds_addr) : "memory", "m0");
 }
 
+// The same load with the LDS destination formed as a wave-uniform scalar
+// base plus a constant, so that no destination holds a scalar register of
+// its own.  The add sets SCC.
+template <uint32_t IMM>
+__device__ __forceinline__ void dma16_si(uint32_t off, const void* base, uint32_t lds_wave) {
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(lds_wave), "i"(IMM) : "memory", "m0", "scc");
+}
+
 // Calls f(integral_constant<int, i>) for i = 0 .. N-1, every index a
 // compile-time constant.
 template <typename F, int... I>

@@ -517,6 +517,8 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
 
   TileDMA<D, STG, NW> dma;
   dma.init(kv_stride, wave, lane);
+  // LDS address of this wave's 1 KB in every stage buffer
+  const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_base + (uint32_t)wave * 1024u);
   LdsRead<D> rd;
   rd.init(lane);
 
@@ -694,26 +696,29 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
     // run meets the workgroup at its own start (stage_period).  Each one
     // meets the workgroup for the next from inside its second sub-step and
     // there issues the loads of the period after that (K stage J+2, V stage
-    // J+1), a full period ahead of their use.  These loads take no branch
-    // (TileDMA::issue_one): a stage past the last key rereads the last row
-    // into a buffer nobody reads.
+    // J+1), a full period ahead of their use.  Those stages either lie wholly
+    // inside the keys or wholly past them (last_steady below keeps a stage
+    // that straddles the last key out of the steady periods), so the loads
+    // take the whole-tile offsets with a scalar base clamped to the last 64
+    // rows: a stage past the end rereads those rows into a buffer nobody
+    // reads.  No vector arithmetic and no branch per load.
     bf16x8 kf0, vf0;
     constexpr int PW = decltype(dma)::PER_WAVE;
-    const uint32_t kv_row_bytes = 2u * (uint32_t)kv_stride;
+    const int last_whole = T.Lk - STG;  // first row of the last 64 keys
     // instruction n of K stage KS (n < PW) or V stage KS - 1 (n >= PW), into
     // K buffer KB and V buffer 2 + VB
     auto load_part = [&](const int KS, auto nc, auto kbuf, auto vbuf)
         __attribute__((always_inline)) {
       constexpr int n = decltype(nc)::value;
       if constexpr (n < PW) {
-        constexpr int KB = decltype(kbuf)::value;
-        const auto src = decltype(dma)::src(T.kbase, kv_stride, KS * STG, T.Lk - 1);
-        dma.template issue_one<n>(src, kv_row_bytes, lds_base + KB * STG_BYTES, wave);
+        constexpr uint32_t KB = decltype(kbuf)::value;
+        const uint16_t* src = T.kbase + (size_t)min(KS * STG, last_whole) * kv_stride;
+        dma16_si<KB * STG_BYTES + (uint32_t)(n * NW) * 1024u>(dma.obytes[n], src, lds_wave);
       } else {
-        constexpr int VB = decltype(vbuf)::value;
-        const auto src = decltype(dma)::src(T.vbase, kv_stride, (KS - 1) * STG, T.Lk - 1);
-        dma.template issue_one<n - PW>(src, kv_row_bytes, lds_base + (2 + VB) * STG_BYTES,
-                                       wave);
+        constexpr uint32_t VB = decltype(vbuf)::value;
+        const uint16_t* src = T.vbase + (size_t)min((KS - 1) * STG, last_whole) * kv_stride;
+        dma16_si<(2 + VB) * STG_BYTES + (uint32_t)((n - PW) * NW) * 1024u>(dma.obytes[n - PW],
+                                                                             src, lds_wave);
       }
     };
     auto steady_period = [&](const int J, auto par, const bool staged, const bool stage_next)
@@ -749,9 +754,13 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
                     next_stage, stage_next);
     };
     // Sub-steps -1 .. n_sub run in periods 0 .. n_stage.  A sub-step j is
-    // steady when 1 <= j <= n_w - 2, so periods 1 .. (n_w - 2) / 2 are.
+    // steady when 1 <= j <= n_w - 2, so periods 1 .. (n_w - 2) / 2 are.  The
+    // steady periods' loads reach K stage last_steady + 1; when the keys end
+    // inside stage n_stage - 1, that stage must be loaded by a general
+    // period, so the steady ones stop at n_stage - 3.
     const int n_period = n_stage + 1;
-    const int last_steady = n_w >= 4 ? (n_w - 2) / 2 : 0;
+    int last_steady = n_w >= 4 ? (n_w - 2) / 2 : 0;
+    if (T.Lk % STG != 0) last_steady = max(0, min(last_steady, n_stage - 3));
     general_period(0);
     // the Q loads are known complete from here on (the first steady period
     // waits for this period's tile loads anyway)
