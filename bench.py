@@ -115,7 +115,7 @@ def kernel_source_hash(unit: str = "fa_fwd.hip", csrc: str = CSRC) -> str:
 # kernel-name pattern -> (traffic.json tag, translation unit)
 TRAFFIC_KERNELS = {
     "fwd_wide_kernel<4, false, false>": ("fwd_noncausal_d128", "fa_fwd_wide.hip"),
-    "fwd_kernel<128, 8, 1, true, true>": ("fwd_causal_d128", "fa_fwd.hip"),
+    "fwd_wide_kernel<4, true, true>": ("fwd_causal_d128", "fa_fwd_wide.hip"),
     "decode_kernel<128>": ("decode_d128", "fa_decode.hip"),
     "bwd_dkdv_kernel<128, false>": ("bwd_dkdv_noncausal_d128", "fa_bwd.hip"),
     "bwd_dq_kernel<128, 4, false>": ("bwd_dq_noncausal_d128", "fa_bwd.hip"),

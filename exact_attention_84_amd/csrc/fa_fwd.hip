@@ -695,20 +695,19 @@ static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Kernel and workgroup shape of a call.  Non-causal plain attention at head
-// dim 128 runs the 64-row-wave kernel: 4 waves (256 rows) for fixed-length
-// batches of at least 1024 queries, else 2 (128 rows: less padding and more
-// workgroups for short or packed sequences).  Causal calls keep the 32-row
-// waves at two waves per SIMD: at the diagonal, where the waves of a
-// workgroup run out of key tiles at different times, the second wave of a
-// SIMD keeps its matrix core busy.  Against the 64-row kernel with its
-// branch-free tile loads and tile loop, these measured 1-4 % faster on the
-// causal workloads (equal on the long GQA one).  The 32-row kernels (also head dim 64, the
-// score variants and FP8) take 8 waves (256 rows, half the K/V loads per
-// query) for fixed-length batches of at least 2048 queries at head dim 128,
-// else 4.
+// Kernel and workgroup shape of a call.  Plain attention at head dim 128,
+// causal or not, runs the 64-row-wave kernel: 4 waves (256 rows) for
+// fixed-length batches of at least 1024 queries, else 2 (128 rows: less
+// padding and more workgroups for short or packed sequences).  Causal calls
+// there pair heavy and light query tiles as the 32-row kernel does; at one
+// wave per SIMD the waves that reach their diagonal first leave their SIMDs
+// idle, and still the kernel measured 3 % faster than the 32-row one on the
+// fixed-length causal workloads and level on the packed one.  The 32-row
+// kernels (head dim 64, the score variants and FP8) take 8 waves (256 rows,
+// half the K/V loads per query) for fixed-length batches of at least 2048
+// queries at head dim 128, else 4.
 FwdPlan fwd_plan(FwdKind kind, int head_dim, bool causal, bool varlen, int seqlen_q) {
-  if (kind == FwdKind::Plain && head_dim == 128 && !causal) {
+  if (kind == FwdKind::Plain && head_dim == 128) {
     const int w = (!varlen && seqlen_q >= 1024) ? 4 : 2;
     return {w, w * 64, 1};
   }
@@ -747,11 +746,12 @@ hipError_t launch_fwd_xf(const FwdParams& p, int head_dim, bool causal, int win_
   return causal ? go(fwd_xf_kernel<64, 4, true>) : go(fwd_xf_kernel<64, 4, false>);
 }
 
+// Plain attention: head dim 64 on the 32-row kernel, head dim 128 on the
+// 64-row kernel (fwd_plan sets p.wide for every such call).
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, hipStream_t stream) {
   if (head_dim == 64) return launch_dw<64, 4>(p, causal, stream);
   if (p.wide) return launch_fwd_wide(p, causal, stream);
-  return p.waves == 8 ? launch_dw<128, 8>(p, causal, stream)
-                      : launch_dw<128, 4>(p, causal, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fa

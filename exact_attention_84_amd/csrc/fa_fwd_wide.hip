@@ -910,8 +910,8 @@ void fwd_wide_kernel(const FwdParams p) {
 
 template __global__ void fwd_wide_kernel<4, false, false>(const FwdParams);
 template __global__ void fwd_wide_kernel<2, false, false>(const FwdParams);
-// Causal calls run the 32-row kernels of fa_fwd.hip: with the diagonal at
-// 64-row granularity these measured 1-4 % slower on the causal workloads.
+template __global__ void fwd_wide_kernel<4, true, true>(const FwdParams);
+template __global__ void fwd_wide_kernel<2, true, true>(const FwdParams);
 
 namespace {
 
@@ -935,12 +935,12 @@ int device_cus() {
 }  // namespace
 
 hipError_t launch_fwd_wide(const FwdParams& p, bool causal, hipStream_t stream) {
-  if (causal) return hipErrorInvalidValue;
   // Each wave takes a whole SIMD, so 4 / waves workgroups fill a compute
-  // unit.  A fixed-length batch, whose tiles all cost the same, launches
-  // just enough workgroups to fill every compute unit once, each taking
-  // every (grid)-th tile, so that a tile's first loads overlap the previous
-  // tile's epilogue.  A multiple of 8 workgroups keeps every tile of a
+  // unit.  A fixed-length batch, whose blocks all cost the same (one tile,
+  // or a causal pair of a heavy and a light tile), launches just enough
+  // workgroups to fill every compute unit once, each taking every (grid)-th
+  // block, so that a tile's first loads overlap the previous tile's
+  // epilogue.  A multiple of 8 workgroups keeps every tile of a
   // workgroup on the same XCD as its block index.  Packed sequences keep one
   // workgroup per tile, which the hardware hands out as compute units free up.
   int grid = p.total;
@@ -950,6 +950,8 @@ hipError_t launch_fwd_wide(const FwdParams& p, bool causal, hipStream_t stream) 
     hipLaunchKernelGGL(kern, dim3(grid), dim3(p.waves * 64), 0, stream, p);
     return hipGetLastError();
   };
+  if (causal)
+    return p.waves == 4 ? go(fwd_wide_kernel<4, true, true>) : go(fwd_wide_kernel<2, true, true>);
   return p.waves == 4 ? go(fwd_wide_kernel<4, false, false>)
                       : go(fwd_wide_kernel<2, false, false>);
 }

@@ -36,7 +36,7 @@ def test_more_than_one_gpu_is_refused():
 
 def test_write_traffic_scales_by_the_copy_kernel(tmp_path, monkeypatch):
     nc = "void fa::fwd_wide_kernel<4, false, false>(fa::FwdParams)"
-    ca = "void fa::fwd_kernel<128, 8, 1, true, true>(fa::FwdParams)"
+    ca = "void fa::fwd_wide_kernel<4, true, true>(fa::FwdParams)"
     cp = "__amd_rocclr_copyBuffer"
     # the copy moves 2^30 bytes each way; FETCH_SIZE reads half of it (x2),
     # WRITE_SIZE all of it (x1), in KiB

@@ -94,7 +94,12 @@ def test_varlen_variants_match_oracle(fa, causal):
 
 def test_window_covering_everything_equals_the_plain_forward(fa):
     """A window wider than the sequence admits every key: the variant kernel
-    must then agree with the plain kernel to rounding."""
+    must then agree with the plain kernel to rounding.  The two kernels are
+    different (64 rows per wave against 32) and round the probabilities to
+    bf16 for the P V product against different references, each within half
+    a bf16 ulp (2^-9 relative) of p; O = sum p v / sum p then differs by at
+    most 2 * 2^-9 * max|v| between them.  Both sum the unrounded fp32 p, so
+    their LSEs differ only by fp32 summation order."""
     import torch
     say("variants wide window")
     q, k, v = W.make_fixed(2, 4, 2, 300, 300, 128, seed=23, wid=WID)
@@ -102,7 +107,8 @@ def test_window_covering_everything_equals_the_plain_forward(fa):
     a = fa.attention(*args, causal=True, out_dtype=torch.float32)
     b = fa.attention(*args, causal=True, window=(10000, 10000), out_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert (a[0] - b[0]).abs().max().item() < 2e-3
+    v_max = float(np.abs(W.bf16_bits_to_f32(v)).max())
+    assert (a[0] - b[0]).abs().max().item() <= 2.0 ** -8 * v_max
     assert (a[1] - b[1]).abs().max().item() < 1e-4
 
 
