@@ -224,6 +224,12 @@ static fa_status fwd_setup(const void* q, const void* k, const void* v, void* o,
   p->wide = plan.wide;
   p->c = scale * fa::kLog2eHost;
   p->o_f32 = o_dtype == FA_DTYPE_F32;
+  const long long gs = (long long)p->group * n_items;  // <= total < 2^31
+  p->fd_items = fa::FastDiv::make((uint32_t)n_items);
+  p->fd_group = fa::FastDiv::make((uint32_t)p->group);
+  p->fd_hkv = fa::FastDiv::make((uint32_t)heads_kv);
+  p->fd_gs = fa::FastDiv::make((uint32_t)gs);
+  p->remap_end = (int)((total / gs) / 8 * 8 * gs);
   return ok();
 }
 

@@ -535,13 +535,21 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
   constexpr int TPB = PAIR ? 2 : 1;
   auto task = [&](const int k, Tile& T) __attribute__((always_inline)) -> bool {
     const int t = blockIdx.x + (k / TPB) * gridDim.x;
-    const int item = xcd_remap(t, p.total, p.group * p.n_items);
-    const int it = item % p.n_items;
-    int rest = item / p.n_items;
-    const int hg = rest % p.group;
-    rest /= p.group;
-    const int kvh = rest % p.hkv;
-    const int b = rest / p.hkv;
+    // xcd_remap with the launch's divisors precomputed (FastDiv)
+    int item = t;
+    if (t < p.remap_end) {
+      const uint32_t slot = (uint32_t)t >> 3;
+      const uint32_t r = p.fd_gs.div(slot);
+      item = (int)((r * 8 + ((uint32_t)t & 7)) * p.fd_gs.d + (slot - r * p.fd_gs.d));
+    }
+    uint32_t rest = p.fd_items.div((uint32_t)item);
+    const int it = item - (int)(rest * p.fd_items.d);
+    uint32_t next = p.fd_group.div(rest);
+    const int hg = (int)(rest - next * p.fd_group.d);
+    rest = next;
+    next = p.fd_hkv.div(rest);
+    const int kvh = (int)(rest - next * p.fd_hkv.d);
+    const int b = (int)next;
     T.h = kvh * p.group + hg;
     int k_start;
     if (p.cu_q) {

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "fa_fastdiv.hpp"
+
 namespace fa {
 
 // Prefill tile shape: 4 or 8 waves per workgroup (fwd_waves), each owning
@@ -39,6 +41,12 @@ struct FwdParams {
   int wide;                // 1: the 64-row-wave kernel (head dim 128), 0: 32-row waves
   float c;                 // scale * log2(e); 1 where scores arrive in log2 units
   int o_f32;
+  // work-item decode of the 64-row kernel by division with precomputed
+  // multipliers: items per (sequence, head), query heads per kv head, kv
+  // heads, and the XCD deal's group size (group * n_items) with the first
+  // block index past its complete rounds of 8 groups
+  FastDiv fd_items, fd_group, fd_hkv, fd_gs;
+  int remap_end;
 };
 
 struct DecodeParams {
