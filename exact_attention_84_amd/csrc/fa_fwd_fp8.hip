@@ -213,6 +213,10 @@ __device__ __forceinline__ bool steady8(State8& st, const char* __restrict__ k_c
     const i32x8 vcur = va;
     if (dt < 3) va = rd.v(v_prev, dt + 1);
     st.o[dt] = mfma_fp8(vcur, pin, st.o[dt]);
+    // keep the product in this slice: without a use here the compiler sinks
+    // the four products past the accept branch below, and the exponentials
+    // then run with the matrix core idle (the asm emits no instruction)
+    asm volatile("" ::"v"(st.o[dt]));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int w = 2 * dt; w < 2 * dt + 2; ++w) {
