@@ -119,7 +119,7 @@ TRAFFIC_KERNELS = {
     "decode_kernel<128>": ("decode_d128", "fa_decode.hip"),
     "bwd_dkdv_kernel<128, false>": ("bwd_dkdv_noncausal_d128", "fa_bwd.hip"),
     "bwd_dq_kernel<128, 4, false>": ("bwd_dq_noncausal_d128", "fa_bwd.hip"),
-    "fwd_fp8_kernel<8, false>": ("fwd_fp8_noncausal_d128", "fa_fwd_fp8.hip"),
+    "fwd_fp8_kernel<4, false>": ("fwd_fp8_noncausal_d128", "fa_fwd_fp8.hip"),
 }
 
 

@@ -669,10 +669,6 @@ void fwd_xf_kernel(const FwdParams p, int win_left, int win_right, float scale, 
 
 // Explicit instantiations: every kernel the dispatcher can launch is emitted
 // on both the device and the host side.
-template __global__ void fwd_kernel<128, 4, kFwdNT, false, false>(const FwdParams);
-template __global__ void fwd_kernel<128, 4, kFwdNT, true, true>(const FwdParams);
-template __global__ void fwd_kernel<128, 8, kFwdNT, false, false>(const FwdParams);
-template __global__ void fwd_kernel<128, 8, kFwdNT, true, true>(const FwdParams);
 template __global__ void fwd_kernel<64, 4, kFwdNT, false, false>(const FwdParams);
 template __global__ void fwd_kernel<64, 4, kFwdNT, true, true>(const FwdParams);
 template __global__ void fwd_local_kernel<128, 4, false>(const FwdParams, int, int);
@@ -703,17 +699,18 @@ static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
 // wave per SIMD the waves that reach their diagonal first leave their SIMDs
 // idle, and still the kernel measured 3 % faster than the 32-row one on the
 // fixed-length causal workloads and level on the packed one.  The 32-row
-// kernels (head dim 64, the score variants and FP8) take 8 waves (256 rows,
-// half the K/V loads per query) for fixed-length batches of at least 2048
-// queries at head dim 128, else 4.
+// kernels (head dim 64, the score variants and FP8) take 4 waves (128 rows),
+// so that two workgroups share a compute unit and the two waves on each SIMD
+// come from different workgroups: not held in step by one workgroup's
+// barriers, one wave's exponentials run beside the other's matrix products.
+// For FP8 that measured 9 % faster than 8-wave workgroups on the
+// B=4 H=16 N=2048 workload (8 waves halve the K/V loads per query).
 FwdPlan fwd_plan(FwdKind kind, int head_dim, bool causal, bool varlen, int seqlen_q) {
   if (kind == FwdKind::Plain && head_dim == 128) {
     const int w = (!varlen && seqlen_q >= 1024) ? 4 : 2;
     return {w, w * 64, 1};
   }
-  if (kind == FwdKind::Ext) return {4, 4 * 32 * kFwdNT, 0};
-  const int w = (head_dim == 128 && !varlen && seqlen_q >= 2048) ? 8 : 4;
-  return {w, w * 32 * kFwdNT, 0};
+  return {4, 4 * 32 * kFwdNT, 0};
 }
 
 template <int D, int NW>

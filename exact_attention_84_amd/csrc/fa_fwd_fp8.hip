@@ -478,16 +478,13 @@ void fwd_fp8_kernel(const FwdParams p, float v_descale) {
 
 template __global__ void fwd_fp8_kernel<4, false>(const FwdParams, float);
 template __global__ void fwd_fp8_kernel<4, true>(const FwdParams, float);
-template __global__ void fwd_fp8_kernel<8, false>(const FwdParams, float);
-template __global__ void fwd_fp8_kernel<8, true>(const FwdParams, float);
 
 hipError_t launch_fwd_fp8(const FwdParams& p, bool causal, float v_descale, hipStream_t stream) {
   auto go = [&](auto kern, int threads) {
     hipLaunchKernelGGL(kern, dim3(p.total), dim3(threads), 0, stream, p, v_descale);
     return hipGetLastError();
   };
-  if (p.waves == 8)
-    return causal ? go(fwd_fp8_kernel<8, true>, 512) : go(fwd_fp8_kernel<8, false>, 512);
+  if (p.waves != 4) return hipErrorInvalidValue;
   return causal ? go(fwd_fp8_kernel<4, true>, 256) : go(fwd_fp8_kernel<4, false>, 256);
 }
 

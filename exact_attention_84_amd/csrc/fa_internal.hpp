@@ -9,8 +9,9 @@
 
 namespace fa {
 
-// Prefill tile shape: 4 or 8 waves per workgroup (fwd_waves), each owning
-// kFwdNT groups of 32 query rows; K/V tiles of 64 keys.
+// Prefill tile shape of the 32-row kernels (head dim 64, the score variants,
+// FP8): 4 waves per workgroup, each owning kFwdNT groups of 32 query rows;
+// K/V tiles of 64 keys.  The 64-row kernel takes 2 or 4 waves of 64 rows.
 #ifndef FA_FWD_NT
 #define FA_FWD_NT 1
 #endif
