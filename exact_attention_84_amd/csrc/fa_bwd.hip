@@ -74,35 +74,6 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const BwdParams p) 
   }
 }
 
-// Stores a wave's 32 columns (lanes) x D rows accumulator, scaled, as rows of
-// `out` ([row][head][d]): lane m32 writes row `row`, head dims dt*32 + 8g +
-// 4hh + 0..3 from registers 4g..4g+3 of block dt.
-template <int D>
-__device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float scale, void* out,
-                                           size_t row_off, int f32, int hh) {
-  if (f32) {
-    float* op = reinterpret_cast<float*>(out) + row_off + 4 * hh;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 w = {acc[dt][4 * g] * scale, acc[dt][4 * g + 1] * scale,
-                         acc[dt][4 * g + 2] * scale, acc[dt][4 * g + 3] * scale};
-        *reinterpret_cast<f32x4*>(op + dt * 32 + 8 * g) = w;
-      }
-  } else {
-    uint16_t* op = reinterpret_cast<uint16_t*>(out) + row_off + 4 * hh;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 w = {pack_bf16x2(acc[dt][4 * g] * scale, acc[dt][4 * g + 1] * scale),
-                         pack_bf16x2(acc[dt][4 * g + 2] * scale, acc[dt][4 * g + 3] * scale)};
-        *reinterpret_cast<u32x2*>(op + dt * 32 + 8 * g) = w;
-      }
-  }
-}
-
 // LDS byte address of a pointer into a __shared__ array, held in a VGPR the
 // compiler cannot see through: operand addresses are then formed as this
 // register plus the lane's offset, with the sub-tile offset folded into the
@@ -391,8 +362,15 @@ void bwd_dq_kernel(const BwdParams p) {
       pv_pf<D, 1>(st.o[0], kc + kt * 64 * D, rd, dsb);  // dQ^T += K^T dS^T
     }
   }
-  if (row_ok)
-    store_rows<D>(st.o[0], p.scale, p.dq, ((size_t)(q_start + qi) * p.hq + h) * D, p.g_f32, hh);
+  // dQ goes out through this wave's part of the K/V stages (free once every
+  // wave is past its last product), as whole 16-byte chunks of row runs
+  __syncthreads();
+  const size_t esz = p.g_f32 ? 4 : 2;
+  char* const stg = wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1;
+  store_rows_lds<D>(st.o[0], p.scale,
+                    reinterpret_cast<char*>(p.dq) + ((size_t)(q_start + qw0) * p.hq + h) * D * esz,
+                    (size_t)p.hq * D * esz, min(Lq, p.rows_cap - q_start) - qw0, p.g_f32 != 0,
+                    stg, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -632,11 +610,18 @@ void bwd_dkdv_kernel(const BwdParams p) {
   if (dp_role) run(std::true_type{});
   else run(std::false_type{});
 
-  if (key_ok) {
-    const size_t off = ((size_t)(k_start + key) * p.hkv + kvh) * D;
-    if (dp_role) store_rows<D>(acc.o[0], p.scale, p.dk, off, p.g_f32, hh);
-    else store_rows<D>(acc.o[0], 1.f, p.dv, off, p.g_f32, hh);
-  }
+  // dV (S waves) and dK (dP waves) go out through LDS that every wave is done
+  // with after the barrier, as whole 16-byte chunks of row runs: 8 KB a wave,
+  // the S waves' in the P exchange area, the dP waves' in the Q and dO stages
+  __syncthreads();
+  const size_t esz = p.g_f32 ? 4 : 2;
+  char* const stg = !dp_role ? reinterpret_cast<char*>(&p_lds[col][0][0][0])
+                    : col < 3 ? &q_lds[0][0] + col * 8192
+                              : &do_lds[0][0];
+  store_rows_lds<D>(acc.o[0], dp_role ? p.scale : 1.f,
+                    reinterpret_cast<char*>(dp_role ? p.dk : p.dv) +
+                        ((size_t)(k_start + kw0) * p.hkv + kvh) * D * esz,
+                    (size_t)p.hkv * D * esz, Lk - kw0, p.g_f32 != 0, stg, lane);
 }
 
 template __global__ void bwd_preprocess_kernel<128>(const BwdParams);

@@ -475,4 +475,72 @@ __device__ __forceinline__ void pv_tile(WaveState<D, NT>& st, const char* __rest
       }
 }
 
+// Stores a wave's 32 rows x D accumulator times `scale` as bf16 or fp32 rows:
+// row r of the wave goes to out + r * row_pitch (bytes), for r < rows.  Lane
+// (m32, hh) holds row m32, values dt*32 + 8g + 4hh + 0..3 in registers
+// 4g .. 4g+3 of acc[dt] (the 32x32 MFMA output layout of O^T-style products).
+// The rows pass through `stg`, this wave's LDS area (32 x 256 bytes; only
+// 32 x 128 for bf16 at D = 64), in pieces of 32 rows x up to 256 bytes, so
+// that every global store writes whole 16-byte chunks of a contiguous run of
+// a row: stores straight from the accumulator layout write 8 bytes per lane,
+// and lines filled by several partial writes cost more.  Row r of a piece
+// holds its chunks XOR-swizzled by r.  The stores are non-temporal: callers
+// write outputs that the same launch does not read.
+template <int D>
+__device__ __forceinline__ void store_rows_lds(const f32x16 (&acc)[D / 32], float scale,
+                                               char* out, size_t row_pitch, int rows, bool f32,
+                                               char* stg, int lane) {
+  static_assert(D == 64 || D == 128, "head dim");
+  const int m32 = lane & 31, hh = lane >> 5;
+  // piece pc of every row: lanes of one row take its 16-byte chunks
+  auto piece_out = [&](auto pw_c, const int pc) __attribute__((always_inline)) {
+    constexpr int PW = decltype(pw_c)::value;  // bytes of a row per piece
+    constexpr int LPR = PW / 16;               // lanes (chunks) per row
+    constexpr int RPI = 64 / LPR;              // rows per instruction
+    constexpr int NI = 32 / RPI;
+    const int c = lane % LPR, r0 = lane / LPR;
+    u32x4 w[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = RPI * i + r0;
+      w[i] = *reinterpret_cast<const u32x4*>(stg + r * PW + ((c ^ (r & (LPR - 1))) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = RPI * i + r0;
+      if (r < rows)
+        __builtin_nontemporal_store(
+            w[i], reinterpret_cast<u32x4*>(out + (size_t)r * row_pitch + PW * pc + 16 * c));
+    }
+  };
+  if (f32) {
+    // 4D bytes a row: pieces of 256 bytes hold head-dim blocks dt = 2 pc, 2 pc + 1
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ch = (dt & 1) * 8 + 2 * g + hh;
+        const f32x4 w = {acc[dt][4 * g] * scale, acc[dt][4 * g + 1] * scale,
+                         acc[dt][4 * g + 2] * scale, acc[dt][4 * g + 3] * scale};
+        *reinterpret_cast<f32x4*>(stg + m32 * 256 + ((ch ^ (m32 & 15)) << 4)) = w;
+      }
+      if (dt & 1) piece_out(std::integral_constant<int, 256>{}, dt >> 1);
+    }
+  } else {
+    // 2D bytes a row, one piece: chunk 4 dt + g, half hh
+    constexpr int PW = 2 * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ch = dt * 4 + g;
+        const u32x2 w = {pack_bf16x2(acc[dt][4 * g] * scale, acc[dt][4 * g + 1] * scale),
+                         pack_bf16x2(acc[dt][4 * g + 2] * scale, acc[dt][4 * g + 3] * scale)};
+        *reinterpret_cast<u32x2*>(stg + m32 * PW + ((ch ^ (m32 & (PW / 16 - 1))) << 4) +
+                                  8 * hh) = w;
+      }
+    piece_out(std::integral_constant<int, PW>{}, 0);
+  }
+}
+
 }  // namespace fa

@@ -581,37 +581,23 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, int win_left, int w
   for (; j <= n_kt; ++j) general_step(j);
 
   // ---- epilogue: O / l, LSE = ln 2 * (r c + log2 l) ----
+  // O goes out through this wave's 8 KB of the K/V stages, free once every
+  // wave is past its last P V, as whole 16-byte chunks of row runs
+  static_assert(NW == 4, "one K/V stage buffer per wave holds its output rows");
+  __syncthreads();
+  char* const stg = wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1;
+  const size_t esz = p.o_f32 ? 4 : 2;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const float lt = halfwave_sum(st.l[t]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lse = lt > 0.f ? (st.mc[t] + __log2f(lt)) * kLn2 : -INFINITY;
     const int qi = qw0 + t * 32 + m32;
-    if (qi < Lq) {
-      const size_t orow = (size_t)(q_start + qi) * p.hq + h;
-      if (p.o_f32) {
-        float* op = reinterpret_cast<float*>(p.o) + orow * D + 4 * hh;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            f32x4 w = {st.o[t][dt][4 * g] * inv, st.o[t][dt][4 * g + 1] * inv,
-                       st.o[t][dt][4 * g + 2] * inv, st.o[t][dt][4 * g + 3] * inv};
-            *reinterpret_cast<f32x4*>(op + dt * 32 + 8 * g) = w;
-          }
-      } else {
-        uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + orow * D + 4 * hh;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            u32x2 w = {pack_bf16x2(st.o[t][dt][4 * g] * inv, st.o[t][dt][4 * g + 1] * inv),
-                       pack_bf16x2(st.o[t][dt][4 * g + 2] * inv, st.o[t][dt][4 * g + 3] * inv)};
-            *reinterpret_cast<u32x2*>(op + dt * 32 + 8 * g) = w;
-          }
-      }
-      if (hh == 0) p.lse[orow] = lse;
-    }
+    if (qi < Lq && hh == 0) p.lse[(size_t)(q_start + qi) * p.hq + h] = lse;
+    const int r0 = qw0 + t * 32;  // the row group's first row
+    store_rows_lds<D>(st.o[t], inv,
+                      reinterpret_cast<char*>(p.o) + ((size_t)(q_start + r0) * p.hq + h) * D * esz,
+                      (size_t)p.hq * D * esz, Lq - r0, p.o_f32 != 0, stg, lane);
   }
   };  // run_tile
 

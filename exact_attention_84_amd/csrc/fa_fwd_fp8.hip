@@ -429,31 +429,16 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdParams& p, float v_descale
     const float lt = halfwave_sum(st.l);
     const float inv = lt > 0.f ? v_descale / lt : 0.f;
     const float lse = lt > 0.f ? (st.mc + __log2f(lt)) * kLn2 : -INFINITY;
-    if (qi < Lq) {
-      const size_t orow = (size_t)(q_start + qi) * p.hq + h;
-      if (p.o_f32) {
-        float* op = reinterpret_cast<float*>(p.o) + orow * kD8 + 4 * hh;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 w = {st.o[dt][4 * g] * inv, st.o[dt][4 * g + 1] * inv,
-                             st.o[dt][4 * g + 2] * inv, st.o[dt][4 * g + 3] * inv};
-            *reinterpret_cast<f32x4*>(op + dt * 32 + 8 * g) = w;
-          }
-      } else {
-        uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + orow * kD8 + 4 * hh;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const u32x2 w = {pack_bf16x2(st.o[dt][4 * g] * inv, st.o[dt][4 * g + 1] * inv),
-                             pack_bf16x2(st.o[dt][4 * g + 2] * inv, st.o[dt][4 * g + 3] * inv)};
-            *reinterpret_cast<u32x2*>(op + dt * 32 + 8 * g) = w;
-          }
-      }
-      if (hh == 0) p.lse[orow] = lse;
-    }
+    if (qi < Lq && hh == 0) p.lse[(size_t)(q_start + qi) * p.hq + h] = lse;
+    // O goes out through 8 KB of the K/V stages, free once every wave is past
+    // its last P V, as whole 16-byte chunks of contiguous row runs
+    __syncthreads();
+    const size_t esz = p.o_f32 ? 4 : 2;
+    store_rows_lds<kD8>(st.o, inv,
+                        reinterpret_cast<char*>(p.o) +
+                            ((size_t)(q_start + qw0) * p.hq + h) * kD8 * esz,
+                        (size_t)p.hq * kD8 * esz, Lq - qw0, p.o_f32 != 0,
+                        wave < 3 ? k_lds + wave * kTile8 : v_lds, lane);
   };  // run_tile
 
   if constexpr (PAIR) {

@@ -814,7 +814,10 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
     // 64 rows are all inside the sequence exists, and its stores test nothing.
     const int rows_left = T.Lq - qw0 - (lane >> 4);
     const bool full = qw0 + 64 <= T.Lq;
-    // rows back out, 16 bytes per lane, 4 rows per wave instruction
+    // rows back out, 16 bytes per lane, 4 rows per wave instruction.  The
+    // stores are non-temporal: O is not read again by this launch, and lines
+    // streamed out of L2 as they are written leave less dirty data for the
+    // write-back at the end of the kernel (measured: 1 µs less per launch).
     auto store_piece = [&](const int t, const int piece) __attribute__((always_inline)) {
       u32x4 w[8];
 #pragma unroll
@@ -825,12 +828,14 @@ __device__ __forceinline__ void wide_body(const FwdParams& p) {
       char* const op = o_lane + (size_t)(32 * t) * o_row + 256 * piece;
       if (full) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(op + (size_t)(4 * i) * o_row) = w[i];
+        for (int i = 0; i < 8; ++i)
+          __builtin_nontemporal_store(w[i], reinterpret_cast<u32x4*>(op + (size_t)(4 * i) * o_row));
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           if (32 * t + 4 * i < rows_left)
-            *reinterpret_cast<u32x4*>(op + (size_t)(4 * i) * o_row) = w[i];
+            __builtin_nontemporal_store(w[i],
+                                        reinterpret_cast<u32x4*>(op + (size_t)(4 * i) * o_row));
       }
     };
     auto read_block = [&](const int b, float (&x)[16]) __attribute__((always_inline)) {

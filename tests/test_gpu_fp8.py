@@ -119,7 +119,7 @@ CASES = [
     (3, 64, 64, 2, 2, False),        # one exact tile
     (1, 1, 1000, 4, 4, False),       # one query
     (2, 1100, 1100, 4, 2, True),     # several causal tile pairs
-    (1, 2048, 2048, 2, 1, True),     # 8-wave workgroups
+    (1, 2048, 2048, 2, 1, True),     # 8 causal pairs of full 128-row tiles
     (1, 2048, 1500, 2, 2, False),
 ]
 
