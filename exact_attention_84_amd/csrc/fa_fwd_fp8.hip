@@ -158,7 +158,11 @@ __device__ __forceinline__ bool softmax8(State8& st, f32x16 (&s)[2], i32x8& pb, 
       pr[e] = fast_exp2(fmaf(s[idx >> 4][idx & 15], c, -msub));
       rs += pr[e];
     }
-    int x = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
+    // the first conversion keeps the high half of its third operand, which
+    // the second overwrites: any register will do, and a dead one saves the
+    // compiler zeroing a fresh one
+    int x =
+        __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], __builtin_bit_cast(int, pr[1]), false);
     x = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], x, true);
     pb[w] = x;
   }
@@ -227,7 +231,10 @@ __device__ __forceinline__ bool steady8(State8& st, const char* __restrict__ k_c
         pr[e] = fast_exp2(fmaf(s[idx >> 4][idx & 15], c, -st.mc));
         rs += pr[e];
       }
-      int x = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
+      // (as in softmax8: the third operand only fills the half that the
+      // second conversion overwrites)
+      int x =
+          __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], __builtin_bit_cast(int, pr[1]), false);
       x = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], x, true);
       pk[w] = x;
       // keep the conversion in this slice
@@ -409,16 +416,18 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdParams& p, float v_descale
     if (wn > 1) {
       general_step(0);
       j = 1;
-      // unrolled by two so that the probability registers swap statically
+      // unrolled by two so that the probability registers swap statically;
+      // no exit between the two halves, which would make the compiler copy
+      // the new probabilities at every step for the exit's sake
 #pragma clang loop unroll(disable)
-      while (j < wn) {
+      while (j + 1 < wn) {
         steady(j, p_a, p_b);
-        ++j;
-        if (j >= wn) {
-          p_a = p_b;  // the generic step expects P_{j-1} in p_a
-          break;
-        }
-        steady(j, p_b, p_a);
+        steady(j + 1, p_b, p_a);
+        j += 2;
+      }
+      if (j < wn) {
+        steady(j, p_a, p_b);
+        p_a = p_b;  // the generic step expects P_{j-1} in p_a
         ++j;
       }
     }
