@@ -53,8 +53,8 @@ FIXED_CASES = [
     (3, 200, 200, 6, 3, 128, True),
     (3, 200, 200, 6, 3, 128, False),
     (5, 130, 130, 4, 4, 64, True),
-    # at least 2048 queries at d=128: 8-wave workgroups of 256 rows, with
-    # ragged tails and Lq != Lk
+    # at least 1024 queries at d=128: 4-wave workgroups of 256 rows (64 per
+    # wave), with ragged tails and Lq != Lk
     (1, 2100, 2100, 2, 1, 128, True),
     (1, 2100, 2100, 2, 1, 128, False),
     (1, 2049, 3000, 2, 2, 128, True),

@@ -6,7 +6,7 @@ The shapes are drawn once from fixed seeds (numpy PCG64), so the case list is
 the same on every run and every case has its own test id.  They mix ragged
 lengths (tails of 1 to 63 rows past a tile), query/key length mismatches,
 empty sequences, grouped heads, both head dims, both output types and, for a
-few cases, lengths long enough for the 8-wave prefill workgroups.  Bounds are
+few cases, lengths long enough for the 256-row prefill workgroups.  Bounds are
 those of the fixed-case tests: max-abs 1e-2 on O (fp32 O; bf16 O adds half a
 bf16 ulp of the exact value), 1e-3 on the natural-log LSE, the same -inf rows;
 the FP8 cases use the bound of test_gpu_fp8.check."""
@@ -26,7 +26,7 @@ def _fixed_cases():
     rng = np.random.default_rng(20261202)
     cases = []
     for i in range(18):
-        long_case = i >= 15                       # 8-wave workgroups (Nq >= 2048, d = 128)
+        long_case = i >= 15                       # 256-row workgroups (Nq >= 1024, d = 128)
         b = 1 if long_case else int(rng.integers(1, 4))
         nq = int(rng.integers(2048, 2600)) if long_case else int(rng.integers(1, 700))
         nk = nq if rng.random() < 0.6 else int(rng.integers(0, 2600 if long_case else 700))
