@@ -412,13 +412,47 @@ __device__ __forceinline__ void fwd_fp8_body(const FwdParams& p, float v_descale
       moved = steady8(st, k_cur, v_prev, rd, pin, pout, alpha, p.c, edge_tile(j),
                       row_lim - j * kBC8);
     };
+    // The same step with its stage S0 = j mod 3 known at compile time, so
+    // that the stage offsets of the operand reads are instruction immediates
+    // instead of a vector add per read base (8 a step).
+    auto steady_s = [&](auto s0c, int j, const i32x8& pin, i32x8& pout)
+        __attribute__((always_inline)) {
+      constexpr int S0 = decltype(s0c)::value;
+      constexpr int S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
+      wait_tiles_upto<PER>((j + 1 < n_kt ? 1 : 0) + (j < n_kt ? 1 : 0));
+      __syncthreads();
+      if (j + 2 < n_kt)
+        dk.issue(kbase, kv_stride, (j + 2) * kBC8, Lk - 1, k_lds + S2 * kTile8, wave);
+      if (j + 1 < n_kt)
+        dv.issue(vbase, kv_stride, (j + 1) * kBC8, Lk - 1, v_lds + S1 * kTile8, wave);
+      rescale();
+      moved = steady8(st, k_lds + S0 * kTile8, v_lds + S2 * kTile8, rd, pin, pout, alpha, p.c,
+                      edge_tile(j), row_lim - j * kBC8);
+    };
     int j = 0;
     if (wn > 1) {
       general_step(0);
       j = 1;
-      // unrolled by two so that the probability registers swap statically;
-      // no exit between the two halves, which would make the compiler copy
-      // the new probabilities at every step for the exit's sake
+      // unrolled by six: the stage (j mod 3) and the probability registers
+      // (j mod 2) are both static; step j = 1 uses stage 1 (the generic step
+      // 0 used stage 0)
+      using C0 = std::integral_constant<int, 0>;
+      using C1 = std::integral_constant<int, 1>;
+      using C2 = std::integral_constant<int, 2>;
+#pragma clang loop unroll(disable)
+      while (j + 5 < wn) {
+        steady_s(C1{}, j, p_a, p_b);
+        steady_s(C2{}, j + 1, p_b, p_a);
+        steady_s(C0{}, j + 2, p_a, p_b);
+        steady_s(C1{}, j + 3, p_b, p_a);
+        steady_s(C2{}, j + 4, p_a, p_b);
+        steady_s(C0{}, j + 5, p_b, p_a);
+        j += 6;
+      }
+      s0 = j % 3;  // the run-time stage of the steps that follow
+      // the rest unrolled by two so that the probability registers swap
+      // statically; no exit between the two halves, which would make the
+      // compiler copy the new probabilities at every step for the exit's sake
 #pragma clang loop unroll(disable)
       while (j + 1 < wn) {
         steady(j, p_a, p_b);
