@@ -205,15 +205,17 @@ __device__ __forceinline__ void scores_pair(f32x16& x, f32x16& y, const char* __
 template <int NKT>
 __device__ __forceinline__ void dq_scores(const f32x16 (&s)[NKT][1], const f32x16 (&dp)[NKT][1],
                                           bf16x8 (&dsb)[NKT][1][2], int lim, bool row_ok,
-                                          float lse2, float dsum, float c) {
+                                          float lse2, float dsum, float c, bool masked = true) {
 #pragma unroll
   for (int kt = 0; kt < NKT; ++kt) {
     float ds[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const bool ok = row_ok && 32 * kt + (v & 3) + 8 * (v >> 2) <= lim;
       const float pe = fast_exp2(fmaf(s[kt][0][v], c, -lse2));
-      ds[v] = ok ? pe * (dp[kt][0][v] - dsum) : 0.f;
+      const float d = pe * (dp[kt][0][v] - dsum);
+      // masked is false only when every row and key of the sub-tiles is
+      // admissible (uniform across the wave), and the selects drop out
+      ds[v] = (!masked || (row_ok && 32 * kt + (v & 3) + 8 * (v >> 2) <= lim)) ? d : 0.f;
     }
     dsb[kt][0][0] = pack_bf16x8(ds);
     dsb[kt][0][1] = pack_bf16x8(ds + 8);
@@ -343,14 +345,19 @@ void bwd_dq_kernel(const BwdParams p) {
   // counter also counts the asm tile loads
   vm_drain();
 
-#pragma clang loop unroll(disable)
-  for (int j = 0; j < n_kt; ++j) {
-    const char* kc = (j & 1) ? k_lds1 : k_lds0;
-    const char* vc = (j & 1) ? v_lds1 : v_lds0;
+  // every row of this wave exists (no row masks); a 32-key sub-tile whose
+  // last key every row of the wave admits then needs no mask at all
+  const bool rows_all = qw0 + 32 <= min(Lq, p.rows_cap - q_start);
+  const int wave_min_key = CAUSAL ? min(Lk - 1, qw0 + delta) : Lk - 1;
+  // Step j: K_j, V_j in stage j & 1.  The loop runs steps in pairs so that
+  // each step's stage buffers are known at compile time (their offsets are
+  // instruction immediates).
+  auto step = [&](const int j, const char* kc, const char* vc, char* kn, char* vn)
+      __attribute__((always_inline)) {
     wait_dma();
     __syncthreads();  // K_j, V_j have landed; everyone is done with the other stage
-    if (j + 1 < n_kt) load_tiles(j + 1, (j & 1) ? k_lds0 : k_lds1, (j & 1) ? v_lds0 : v_lds1);
-    if (qw0 >= Lq) continue;  // this wave has no rows (uniform)
+    if (j + 1 < n_kt) load_tiles(j + 1, kn, vn);
+    if (qw0 >= Lq) return;  // this wave has no rows (uniform)
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int ksub = j * BC + 32 * kt;
@@ -358,10 +365,21 @@ void bwd_dq_kernel(const BwdParams p) {
       f32x16 s[1][1], dp[1][1];
       scores_pair<D>(s[0][0], dp[0][0], kc + kt * 64 * D, vc + kt * 64 * D, rd, st.qf[0], dof[0]);
       bf16x8 dsb[1][1][2];
-      dq_scores<1>(s, dp, dsb, row_lim - ksub, row_ok, lse2, dsum, p.c);
+      const bool masked = !rows_all || ksub + 31 > wave_min_key;
+      if (masked)
+        dq_scores<1>(s, dp, dsb, row_lim - ksub, row_ok, lse2, dsum, p.c, true);
+      else
+        dq_scores<1>(s, dp, dsb, row_lim - ksub, row_ok, lse2, dsum, p.c, false);
       pv_pf<D, 1>(st.o[0], kc + kt * 64 * D, rd, dsb);  // dQ^T += K^T dS^T
     }
+  };
+  int j = 0;
+#pragma clang loop unroll(disable)
+  for (; j + 1 < n_kt; j += 2) {
+    step(j, k_lds0, v_lds0, k_lds1, v_lds1);
+    step(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);
   }
+  if (j < n_kt) step(j, k_lds0, v_lds0, k_lds1, v_lds1);
   // dQ goes out through this wave's part of the K/V stages (free once every
   // wave is past its last product), as whole 16-byte chunks of row runs
   __syncthreads();
