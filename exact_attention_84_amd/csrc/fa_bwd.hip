@@ -569,20 +569,26 @@ void bwd_dkdv_kernel(const BwdParams p) {
             const int lo = key - delta - qsub - 4 * hh;  // first admissible row offset (causal)
             const int hi = lq_eff - 1 - qsub - 4 * hh;   // last row offset with data
             float pe[16];
+            auto probs = [&](const bool masked) __attribute__((always_inline)) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const f32x4 l2 = *reinterpret_cast<const f32x4*>(stl + 32 * kt + 8 * g + 4 * hh);
+              for (int g = 0; g < 4; ++g) {
+                const f32x4 l2 = *reinterpret_cast<const f32x4*>(stl + 32 * kt + 8 * g + 4 * hh);
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                pe[4 * g + e] = fast_exp2(fmaf(x[kt][0][4 * g + e], p.c, -l2[e]));
-            }
-            if (!full) {  // edge tile (uniform per wave)
-#pragma unroll
-              for (int v = 0; v < 16; ++v) {
-                const int r = (v & 3) + 8 * (v >> 2);
-                pe[v] = (r <= hi && (!CAUSAL || r >= lo)) ? pe[v] : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                  const int r = (e & 3) + 8 * g;  // row offset of element 4 g + e
+                  const float v = fast_exp2(fmaf(x[kt][0][4 * g + e], p.c, -l2[e]));
+                  pe[4 * g + e] =
+                      (!masked || (r <= hi && (!CAUSAL || r >= lo))) ? v : 0.f;
+                }
               }
-            }
+            };
+            // two paths on the uniform edge test, so that interior tiles
+            // carry no per-element selects (folded into one path, the
+            // compiler made every tile pay for them)
+            if (full)
+              probs(false);
+            else
+              probs(true);
 #pragma unroll
             for (int g = 0; g < 4; ++g)
               p_lds[col][kt][g][lane] =
