@@ -542,6 +542,9 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, int win_left, int w
       lim[t] = row_lim[t] - (kt0 + jj) * BC;
       lo[t] = row_lo[t] - (kt0 + jj) * BC;
       rel[t] = row_rel[t] - (kt0 + jj) * BC;
+      // opaque per step: otherwise the compiler carries every element's
+      // mask threshold from step to step, paying for it on unmasked steps
+      asm volatile("" : "+v"(lim[t]), "+v"(lo[t]));
     }
     if constexpr (XF)
       moved = steady_step_max_first<D, NT, LOCAL, XF>(st, k_cur, v_prev, rd, pin, pout, alpha,
