@@ -174,6 +174,35 @@ __device__ __forceinline__ void pv_pf(f32x16 (&acc)[D / 32], const char* __restr
   }
 }
 
+// pv_pf with the tile's transposed-read bases computed once by the caller;
+// `off` (a compile-time constant where it is called) selects the stage and
+// lands in the instructions' immediates.
+template <int D, int NKT>
+__device__ __forceinline__ void pv_pf_at(f32x16 (&acc)[D / 32], const VBases<D>& vb, uint32_t off,
+                                         const bf16x8 (&pb)[NKT][1][2]) {
+  constexpr int DT = D / 32;
+  constexpr int N = NKT * 2 * DT;
+  bf16x8 op[3];
+  auto read = [&](int i) {
+    const int kt = i / (2 * DT), u = (i / DT) & 1, dt = i % DT;
+    const uint32_t row = off + (kt * 32 + 16 * u) * 2 * D;
+    const s16x4b lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4b*)(uintptr_t)(vb.b[dt][0] + row));
+    const s16x4b hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4b*)(uintptr_t)(vb.b[dt][1] + row));
+    const s16x8b w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, w);
+  };
+  op[0] = read(0);
+  op[1] = read(1);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + 2 < N) op[(i + 2) % 3] = read(i + 2);
+    const int kt = i / (2 * DT), u = (i / DT) & 1, dt = i % DT;
+    acc[dt] = mfma_32x32x16(op[i % 3], pb[kt][0][u], acc[dt]);
+  }
+}
+
 // Two independent 32 x 32 score products over the head dimension, their
 // MFMA chains interleaved: x = A_x B_x^T and y = A_y B_y^T with A_x, A_y rows
 // of swizzled LDS tiles and B_x, B_y fragments in registers.  Operands are
@@ -187,6 +216,30 @@ __device__ __forceinline__ void scores_pair(f32x16& x, f32x16& y, const char* __
   const KBases<D> kx(lds_base(ax), rd), ky(lds_base(ay), rd);
   bf16x8 op[3];
   auto read = [&](int i) { return (i & 1) ? ky.read(0, i >> 1) : kx.read(0, i >> 1); };
+  op[0] = read(0);
+  op[1] = read(1);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + 2 < N) op[(i + 2) % 3] = read(i + 2);
+    const int st = i >> 1;
+    if (i & 1) y = mfma_32x32x16(op[i % 3], by[st], st == 0 ? f32x16{} : y);
+    else x = mfma_32x32x16(op[i % 3], bx[st], st == 0 ? f32x16{} : x);
+  }
+}
+
+// scores_pair with both tiles read through one set of bases computed once
+// by the caller, at offsets ox and oy (compile-time constants where it is
+// called, so they land in the instructions' immediates).
+template <int D>
+__device__ __forceinline__ void scores_pair_at(f32x16& x, f32x16& y, const KBases<D>& kb,
+                                               uint32_t ox, uint32_t oy,
+                                               const bf16x8 (&bx)[D / 16],
+                                               const bf16x8 (&by)[D / 16]) {
+  constexpr int N = 2 * (D / 16);  // MFMAs, alternating x and y
+  bf16x8 op[3];
+  auto read = [&](int i) {
+    return lds_load<bf16x8>(kb.b[i >> 1] + ((i & 1) ? oy : ox));
+  };
   op[0] = read(0);
   op[1] = read(1);
 #pragma unroll
@@ -235,10 +288,13 @@ void bwd_dq_kernel(const BwdParams p) {
   constexpr int BR = NW * 32;
   constexpr int TILE = BC * D * 2;
   constexpr int KS = D / 16;
-  __shared__ __attribute__((aligned(1024))) char k_lds0[TILE];
-  __shared__ __attribute__((aligned(1024))) char k_lds1[TILE];
-  __shared__ __attribute__((aligned(1024))) char v_lds0[TILE];
-  __shared__ __attribute__((aligned(1024))) char v_lds1[TILE];
+  // K stages 0 and 1, then V stages 0 and 1, in one array so that a stage is
+  // a constant offset from one set of per-lane read bases
+  __shared__ __attribute__((aligned(1024))) char kv_lds[4 * TILE];
+  char* const k_lds0 = kv_lds;
+  char* const k_lds1 = kv_lds + TILE;
+  char* const v_lds0 = kv_lds + 2 * TILE;
+  char* const v_lds1 = kv_lds + 3 * TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -352,7 +408,11 @@ void bwd_dq_kernel(const BwdParams p) {
   // Step j: K_j, V_j in stage j & 1.  The loop runs steps in pairs so that
   // each step's stage buffers are known at compile time (their offsets are
   // instruction immediates).
-  auto step = [&](const int j, const char* kc, const char* vc, char* kn, char* vn)
+  // per-lane read bases of the whole array, computed once: the score reads
+  // (K and V tiles alike) and the transposed reads of K
+  const KBases<D> kbase_rd(lds_base(kv_lds), rd);
+  const VBases<D> vbase_rd(lds_base(kv_lds), rd);
+  auto step = [&](const int j, const uint32_t ko, const uint32_t vo, char* kn, char* vn)
       __attribute__((always_inline)) {
     wait_dma();
     __syncthreads();  // K_j, V_j have landed; everyone is done with the other stage
@@ -363,23 +423,24 @@ void bwd_dq_kernel(const BwdParams p) {
       const int ksub = j * BC + 32 * kt;
       if (ksub > wave_last_key) break;  // past this wave's keys (uniform)
       f32x16 s[1][1], dp[1][1];
-      scores_pair<D>(s[0][0], dp[0][0], kc + kt * 64 * D, vc + kt * 64 * D, rd, st.qf[0], dof[0]);
+      scores_pair_at<D>(s[0][0], dp[0][0], kbase_rd, ko + kt * 64 * D, vo + kt * 64 * D, st.qf[0],
+                        dof[0]);
       bf16x8 dsb[1][1][2];
       const bool masked = !rows_all || ksub + 31 > wave_min_key;
       if (masked)
         dq_scores<1>(s, dp, dsb, row_lim - ksub, row_ok, lse2, dsum, p.c, true);
       else
         dq_scores<1>(s, dp, dsb, row_lim - ksub, row_ok, lse2, dsum, p.c, false);
-      pv_pf<D, 1>(st.o[0], kc + kt * 64 * D, rd, dsb);  // dQ^T += K^T dS^T
+      pv_pf_at<D, 1>(st.o[0], vbase_rd, ko + kt * 64 * D, dsb);  // dQ^T += K^T dS^T
     }
   };
   int j = 0;
 #pragma clang loop unroll(disable)
   for (; j + 1 < n_kt; j += 2) {
-    step(j, k_lds0, v_lds0, k_lds1, v_lds1);
-    step(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+    step(j, 0, 2 * TILE, k_lds1, v_lds1);
+    step(j + 1, TILE, 3 * TILE, k_lds0, v_lds0);
   }
-  if (j < n_kt) step(j, k_lds0, v_lds0, k_lds1, v_lds1);
+  if (j < n_kt) step(j, 0, 2 * TILE, k_lds1, v_lds1);
   // dQ goes out through this wave's part of the K/V stages (free once every
   // wave is past its last product), as whole 16-byte chunks of row runs
   __syncthreads();
